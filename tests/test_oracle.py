@@ -1,0 +1,354 @@
+"""Pins for the fp64 CPU oracle (CPU only).
+
+The oracle is pinned to things other than itself: library routines (numpy
+dgemm, torch's scaled_dot_product_attention and float8_e4m3fn casts), closed
+forms and invariants of softmax attention, and 50-digit decimal brute force
+on tiny inputs. Each pin is chosen so that a plausible slip in the oracle (a
+dropped scale, a wrong index, a transposed operand, a missing max-shift or
+normalisation) fails at least one of them.
+"""
+import decimal
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BF16, FP8 = oracle.KV_BF16, oracle.KV_FP8
+
+
+def _torch_decode_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def _torch_decode_e4m3(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ------------------------------------------------------------------ formats
+
+def test_e4m3_table_matches_torch():
+    t = oracle.e4m3_table()
+    ref = _torch_decode_e4m3(np.arange(256, dtype=np.uint8))
+    same = (t == ref) | (np.isnan(t) & np.isnan(ref))
+    assert same.all(), np.nonzero(~same)
+
+
+def test_e4m3_golden_values():
+    # OCP 8-bit floating point specification (OFP8), E4M3 encoding table
+    with open(os.path.join(GOLDEN, "e4m3_ocp_values.json")) as f:
+        g = json.load(f)
+    for code_hex, val in g["values"].items():
+        got = oracle.decode_e4m3(np.array([int(code_hex, 16)], dtype=np.uint8))[0]
+        if val == "nan":
+            assert math.isnan(got), code_hex
+        else:
+            assert got == float(val), (code_hex, got, val)
+    t = oracle.e4m3_table()
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)               # finite positive codes increase
+    assert np.all(t[0x80:0xFF] == -t[:0x7F])      # sign bit is a pure sign
+
+
+def test_bf16_decode_matches_torch():
+    bits = np.random.default_rng(5).integers(0, 1 << 16, size=20000, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]       # drop inf/nan patterns
+    assert np.array_equal(oracle.decode_bf16(bits), _torch_decode_bf16(bits))
+
+
+def test_generator_encoders_match_torch():
+    a = np.random.default_rng(7).standard_normal(50000).astype(np.float32)
+    for s in (1e-3, 1.0, 40.0):
+        x = (a * s).astype(np.float32)
+        ref = torch.from_numpy(x).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(synth.e4m3_codes(x), ref)
+    assert np.array_equal(synth.bf16_bits(a),
+                          torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    # saturation instead of NaN
+    assert synth.e4m3_codes(np.array([1e6, -1e6], dtype=np.float32)).tolist() == [0x7E, 0xFE]
+
+
+# ------------------------------------------------------------------ attention
+
+def _small_case(B=2, L=(37, 70), kv="bf16", seed=3, paged=False, q_std=1.0):
+    return synth.make_case("t", B, list(L), kv, seed=seed, paged=paged, q_std=q_std)
+
+
+def _kv_decoded(case):
+    dec = oracle.decode_bf16 if case.kv_dtype == "bf16" else oracle.decode_e4m3
+    return dec(case.k) * case.k_scale, dec(case.v) * case.v_scale
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_matches_torch_sdpa_mqa(kv):
+    """MQA structure: one shared K/V head broadcast to all 64 query heads is
+    textbook per-head softmax attention (torch SDPA, float64, CPU)."""
+    case = _small_case(kv=kv)
+    q = oracle.case_q(case)
+    o, lse = oracle.case_attention(case)
+    K, V = _kv_decoded(case)
+    for b in range(case.batch):
+        L = int(case.seq_lens[b])
+        qt = torch.from_numpy(q[b])[None]                              # [1, H, D] as [B, L=H, D]
+        kt = torch.from_numpy(K[b, :L])[None]
+        vt = torch.from_numpy(V[b, :L])[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=1.0 / 16)[0]
+        assert _rel(o[b], ref.numpy()) < 1e-12
+        s = (torch.from_numpy(q[b]) @ torch.from_numpy(K[b, :L]).T) / 16.0
+        assert np.max(np.abs(lse[b] - torch.logsumexp(s, dim=1).numpy())) < 1e-12
+
+
+def test_weights_sum_to_one():
+    case = _small_case(L=(1, 4096), seed=11)
+    q = oracle.case_q(case)
+    for b, h in [(0, 0), (1, 5), (1, 63)]:
+        w = oracle.weights(q, case.k, case.seq_lens, b, h, kv_dtype=BF16)
+        assert len(w) == case.seq_lens[b]
+        assert abs(w.sum() - 1.0) < 1e-12
+        assert (w >= 0).all()
+
+
+def test_identical_keys_give_mean_v():
+    case = _small_case(L=(50, 129), seed=12)
+    case.k[:] = case.k[:, :1, :]                  # every row = row 0
+    o, _ = oracle.case_attention(case)
+    _, V = _kv_decoded(case)
+    for b in range(case.batch):
+        L = int(case.seq_lens[b])
+        mean = V[b, :L].mean(axis=0)
+        assert np.max(np.abs(o[b] - mean[None, :])) < 1e-13
+
+
+def test_one_token_returns_v_exactly():
+    case = _small_case(L=(1, 1), kv="fp8", seed=13)
+    q = oracle.case_q(case)
+    o, lse = oracle.case_attention(case)
+    K, V = _kv_decoded(case)
+    for b in range(case.batch):
+        assert np.array_equal(o[b], np.broadcast_to(V[b, 0], o[b].shape))
+        assert np.allclose(lse[b], (q[b] @ K[b, 0]) / 16.0, rtol=0, atol=1e-13)
+
+
+def test_permutation_invariance():
+    case = _small_case(L=(200, 333), seed=14)
+    o, lse = oracle.case_attention(case)
+    rng = np.random.default_rng(99)
+    for b in range(case.batch):
+        L = int(case.seq_lens[b])
+        p = rng.permutation(L)
+        case.k[b, :L] = case.k[b, p]
+        case.v[b, :L] = case.v[b, p]
+    o2, lse2 = oracle.case_attention(case)
+    assert _rel(o2, o) < 1e-13
+    assert np.max(np.abs(lse2 - lse)) < 1e-12
+
+
+def test_scale_zero_gives_mean_v():
+    case = _small_case(L=(17, 301), seed=15)
+    case.softmax_scale = 0.0
+    o, lse = oracle.case_attention(case)
+    _, V = _kv_decoded(case)
+    for b in range(case.batch):
+        L = int(case.seq_lens[b])
+        assert np.max(np.abs(o[b] - V[b, :L].mean(axis=0)[None])) < 1e-13
+        assert np.allclose(lse[b], math.log(L), rtol=0, atol=1e-13)
+
+
+def test_dominant_key_returns_its_v_row():
+    case = _small_case(B=1, L=(64,), seed=16)
+    q = np.zeros((1, 64, 256))
+    q[0, :, 0] = 1.0
+    K = np.zeros((1, case.k.shape[1], 256), dtype=np.float32)
+    K[0, :, 0] = 0.5
+    K[0, 23, 0] = 0.5 + 60.0 * 16.0                # logit +60 above the rest
+    case.k = synth.bf16_bits(K)
+    o, _ = oracle.attention(q, case.k, case.v, case.seq_lens, kv_dtype=BF16)
+    _, V = _kv_decoded(case)
+    assert np.max(np.abs(o[0] - V[0, 23][None])) < 1e-20
+
+
+def test_empty_sequence():
+    case = _small_case(L=(0, 5), seed=17)
+    o, lse = oracle.case_attention(case)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.all(np.isfinite(lse[1]))
+
+
+def _decimal_attention(q, K, V, scale):
+    decimal.getcontext().prec = 50
+    Dd = decimal.Decimal
+    H, D = q.shape
+    L = K.shape[0]
+    o = np.zeros((H, D))
+    lse = np.zeros(H)
+    for h in range(H):
+        s = [Dd(scale) * sum(Dd(float(q[h, d])) * Dd(float(K[t, d])) for d in range(D))
+             for t in range(L)]
+        m = max(s)
+        e = [(x - m).exp() for x in s]
+        tot = sum(e)
+        for d in range(D):
+            o[h, d] = float(sum(e[t] / tot * Dd(float(V[t, d])) for t in range(L)))
+        lse[h] = float(m + tot.ln())
+    return o, lse
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_tiny_brute_force_decimal(kv):
+    rng = np.random.default_rng(21)
+    for trial in range(6):
+        H, D, L = int(rng.integers(1, 4)), int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        q = synth.bf16_bits(rng.standard_normal((1, H, D)).astype(np.float32) * 3)
+        qd = _torch_decode_bf16(q)
+        Kf = rng.standard_normal((1, L, D)).astype(np.float32) * 2
+        Vf = rng.standard_normal((1, L, D)).astype(np.float32)
+        if kv == "bf16":
+            K, V, ks, vs, code = synth.bf16_bits(Kf), synth.bf16_bits(Vf), 1.0, 1.0, BF16
+            Kd, Vd = _torch_decode_bf16(K), _torch_decode_bf16(V)
+        else:
+            K, V, ks, vs, code = synth.e4m3_codes(Kf), synth.e4m3_codes(Vf), 0.375, 1.25, FP8
+            Kd, Vd = _torch_decode_e4m3(K) * ks, _torch_decode_e4m3(V) * vs
+        scale = 0.7
+        o, lse = oracle.attention(qd, K, V, np.array([L], np.int32), kv_dtype=code,
+                                  k_scale=ks, v_scale=vs, softmax_scale=scale)
+        ro, rl = _decimal_attention(qd[0], Kd[0], Vd[0], scale)
+        assert np.max(np.abs(o[0] - ro)) <= 1e-14 * max(1.0, np.max(np.abs(ro)))
+        assert np.max(np.abs(lse[0] - rl)) <= 1e-14 * max(1.0, np.max(np.abs(rl)))
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 512])
+def test_split_equals_unsplit(chunk):
+    case = _small_case(L=(1000, 513), seed=22, kv="fp8")
+    o, lse = oracle.case_attention(case)
+    o2, lse2 = oracle.case_attention(case, chunk=chunk)
+    assert _rel(o2, o) < 1e-13
+    assert np.max(np.abs(lse2 - lse)) < 1e-12
+
+
+def test_paged_equals_contiguous_bitwise():
+    """Same logical data through a permuted page table gives identical fp64
+    results (the same operations in the same order)."""
+    pc = synth.make_case("p", 3, [64, 130, 1], "fp8", seed=23, paged=True)
+    P = pc.k.shape[0]
+    maxL = int(pc.seq_lens.max())
+    kc = np.zeros((3, maxL, 256), np.uint8)
+    vc = np.zeros((3, maxL, 256), np.uint8)
+    for b in range(3):
+        for t in range(int(pc.seq_lens[b])):
+            p = pc.page_table[b, t // 64]
+            kc[b, t] = pc.k[p, t % 64]
+            vc[b, t] = pc.v[p, t % 64]
+    q = oracle.case_q(pc)
+    o1, l1 = oracle.case_attention(pc)
+    o2, l2 = oracle.attention(q, kc, vc, pc.seq_lens, kv_dtype=FP8, k_scale=pc.k_scale,
+                              v_scale=pc.v_scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert P == 1 + 3 + 1
+
+
+def test_gather_matches_numpy_indexing():
+    pc = synth.make_case("p", 4, [1, 63, 64, 200], "bf16", seed=24, paged=True)
+    for b in range(4):
+        L = int(pc.seq_lens[b])
+        t = np.arange(L)
+        pages = pc.page_table[b, t // 64]
+        kd, vd = oracle.gather_kv(pc.k, pc.v, pc.seq_lens, b, page_table=pc.page_table)
+        assert np.array_equal(kd, pc.k[pages, t % 64])
+        assert np.array_equal(vd, pc.v[pages, t % 64])
+
+
+def test_page_table_is_permutation():
+    c = synth.config_case(4, batch=24, scale_len=1 / 16)
+    npg = (c.seq_lens + 63) // 64
+    used = np.concatenate([c.page_table[b, :npg[b]] for b in range(c.batch)])
+    assert np.array_equal(np.sort(used), np.arange(c.k.shape[0]))
+    assert c.seq_lens.min() >= 64 and c.seq_lens.max() <= 512
+
+
+# ------------------------------------------------------------------ Q projection
+
+def _tiny_qproj_inputs(B, hidden, rank, nq, seed):
+    rng = np.random.default_rng(seed)
+    x = synth.bf16_bits(rng.standard_normal((B, hidden)).astype(np.float32))
+    wa = synth.bf16_bits((rng.standard_normal((hidden, rank)) / math.sqrt(hidden)).astype(np.float32))
+    wb = synth.bf16_bits((rng.standard_normal((rank, nq)) / math.sqrt(rank)).astype(np.float32))
+    g = synth.bf16_bits((1.0 + 0.25 * rng.standard_normal(rank)).astype(np.float32))
+    return x, wa, g, wb
+
+
+def test_qproj_matches_numpy_dgemm():
+    x, wa, g, wb = _tiny_qproj_inputs(5, 96, 48, 80, 31)
+    q, c, chat = oracle.qproj(x, wa, g, wb, eps=1e-6, return_c=True)
+    X, WA, G, WB = (_torch_decode_bf16(a) for a in (x, wa, g, wb))
+    c_ref = X @ WA                                       # library dgemm
+    assert _rel(c, c_ref) < 1e-13
+    q_ref = chat @ WB
+    assert _rel(q, q_ref) < 1e-13
+    # chat is c scaled per row by a positive factor times gamma
+    ratio = chat / (c * G[None, :])
+    assert np.allclose(ratio, ratio[:, :1], rtol=1e-13, atol=0)
+
+
+def test_rmsnorm_closed_form_and_gamma():
+    x, wa, g, wb = _tiny_qproj_inputs(4, 64, 32, 16, 32)
+    ones = synth.bf16_bits(np.ones(32, np.float32))
+    eps = 1e-3
+    _, c, chat = oracle.qproj(x, wa, ones, wb, eps=eps, return_c=True)
+    m = (c * c).mean(axis=1)
+    assert np.allclose((chat * chat).sum(axis=1), 32 * m / (m + eps), rtol=1e-13, atol=0)
+    twos = synth.bf16_bits(np.full(32, 2.0, np.float32))
+    _, _, chat2 = oracle.qproj(x, wa, twos, wb, eps=eps, return_c=True)
+    assert np.array_equal(chat2, 2 * chat)
+
+
+def test_rmsnorm_scale_invariance_exact():
+    """With eps = 0, scaling x by 4 (exact in bf16 and fp64) leaves chat and q
+    bit-identical: the norm divides the scale out."""
+    x, wa, g, wb = _tiny_qproj_inputs(3, 64, 32, 24, 33)
+    x4 = synth.bf16_bits(_torch_decode_bf16(x).astype(np.float32) * 4)
+    q1 = oracle.qproj(x, wa, g, wb, eps=0.0)
+    q4 = oracle.qproj(x4, wa, g, wb, eps=0.0)
+    assert np.array_equal(q1, q4)
+    qe = oracle.qproj(x, wa, g, wb, eps=1e-6)
+    assert not np.array_equal(q1, qe) and _rel(qe, q1) < 1e-5
+
+
+def test_qproj_tiny_decimal():
+    decimal.getcontext().prec = 50
+    Dd = decimal.Decimal
+    x, wa, g, wb = _tiny_qproj_inputs(2, 8, 4, 6, 34)
+    X, WA, G, WB = (_torch_decode_bf16(a) for a in (x, wa, g, wb))
+    eps = 1e-6
+    q = oracle.qproj(x, wa, g, wb, eps=eps)
+    for b in range(2):
+        c = [sum(Dd(float(X[b, i])) * Dd(float(WA[i, j])) for i in range(8)) for j in range(4)]
+        r = 1 / (sum(v * v for v in c) / 4 + Dd(eps)).sqrt()
+        ch = [c[j] * r * Dd(float(G[j])) for j in range(4)]
+        for n in range(6):
+            ref = float(sum(ch[j] * Dd(float(WB[j, n])) for j in range(4)))
+            assert abs(q[b, n] - ref) <= 1e-14 * max(1.0, abs(ref))
+
+
+def test_config_recipes():
+    c1 = synth.config_case(1)
+    assert c1.q.shape == (1, 64, 256) and c1.k.shape == (1, 256, 256) and c1.kv_dtype == "bf16"
+    c3 = synth.config_case(3, batch=2, scale_len=1 / 64)
+    assert c3.kv_dtype == "fp8" and c3.k.dtype == np.uint8 and 0 < c3.k_scale < 1
+    c5 = synth.config_case(5, batch=4, scale_len=1 / 256)
+    assert c5.seq_lens.tolist() == [128, 128, 256, 256] and c5.split_tokens == 512
+    c2 = synth.config_case(2, batch=2, scale_len=1 / 256)
+    assert c2.x.shape == (2, 7168) and c2.w_qa.shape == (7168, 2048) and c2.w_qb.shape == (2048, 16384)
+    # seeded: same seed, same bytes
+    assert np.array_equal(synth.config_case(1).k, c1.k)
