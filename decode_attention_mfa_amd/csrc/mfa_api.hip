@@ -1,0 +1,282 @@
+// mfa_api.hip -- the C ABI declared in include/mfa.h: argument checks,
+// workspace ownership, split selection and kernel launches. Every check runs
+// on the host before anything is enqueued; no call synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "mfa.h"
+#include "mfa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(MFA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr uint32_t kMagic = 0x4d464131u;   // "MFA1"
+constexpr uint32_t kDead = 0xdeadbeefu;
+constexpr int kMinAutoSplit = 256;
+constexpr int kMaxAutoSplit = 2048;
+
+}  // namespace
+
+struct mfa_ctx {
+    uint32_t magic;
+    mfa_config cfg;
+    int device;
+    int num_cu;
+    int max_chunks;        // per sequence, at the smallest chunk this handle may use
+    float* part_o;         // [max_batch * max_chunks][64][256]
+    float* part_lse;       // [max_batch * max_chunks][64]
+    float* c_part;         // [kQprojSplit][max_batch][q_rank]
+    uint16_t* chat;        // [max_batch][q_rank]
+};
+
+static bool valid_handle(mfa_handle h) { return h != nullptr && h->magic == kMagic; }
+
+static int round_up(int64_t a, int64_t m) { return (int)(((a + m - 1) / m) * m); }
+
+static int32_t choose_split(const mfa_ctx* h, int32_t batch, int32_t max_len) {
+    if (h->cfg.split_tokens > 0) return h->cfg.split_tokens;
+    if (max_len <= 0) return kMinAutoSplit;
+    // one chunk per compute unit's share of the batch's tokens, whole pages
+    int64_t share = ((int64_t)batch * max_len + h->num_cu - 1) / h->num_cu;
+    int64_t c = round_up(share, mfa::kStep);
+    if (c < kMinAutoSplit) c = kMinAutoSplit;
+    if (c > kMaxAutoSplit) c = kMaxAutoSplit;
+    if (c > round_up(max_len, mfa::kStep)) c = round_up(max_len, mfa::kStep);
+    return (int32_t)c;
+}
+
+extern "C" {
+
+const char* mfa_status_string(int status) {
+    switch (status) {
+        case MFA_OK: return "ok";
+        case MFA_ERR_INVALID: return "invalid argument";
+        case MFA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MFA_ERR_NOMEM: return "out of device memory";
+        case MFA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* mfa_last_error(void) { return g_last_error; }
+
+int mfa_create(const mfa_config* cfg, mfa_handle* out) {
+    g_last_error[0] = 0;
+    if (!cfg || !out) return fail(MFA_ERR_INVALID, "mfa_create: null cfg or out");
+    *out = nullptr;
+    const mfa_config c = *cfg;
+    if (c.num_heads != mfa::kHeads || c.head_dim != mfa::kHeadDim)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: only 64 heads x 256 are supported (got %d x %d)",
+                    c.num_heads, c.head_dim);
+    if (c.hidden <= 0 || c.hidden % (64 * mfa::kQprojSplit) != 0)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: hidden must be a positive multiple of %d (got %d)",
+                    64 * mfa::kQprojSplit, c.hidden);
+    if (c.q_rank <= 0 || c.q_rank % 64 != 0 || c.q_rank > 65536)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: q_rank must be a positive multiple of 64 (got %d)",
+                    c.q_rank);
+    if (c.kv_dtype != MFA_DTYPE_BF16 && c.kv_dtype != MFA_DTYPE_FP8_E4M3)
+        return fail(MFA_ERR_INVALID, "mfa_create: bad kv_dtype %d", c.kv_dtype);
+    if (c.page_size != 0 && c.page_size != mfa::kPage)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: page_size must be 0 or 64 (got %d)", c.page_size);
+    if (c.max_batch < 1 || c.max_context < 1)
+        return fail(MFA_ERR_INVALID, "mfa_create: max_batch and max_context must be >= 1");
+    if (c.split_tokens < 0 || c.split_tokens % mfa::kStep != 0)
+        return fail(MFA_ERR_INVALID, "mfa_create: split_tokens must be 0 or a positive multiple of 64 (got %d)",
+                    c.split_tokens);
+    if (!(c.softmax_scale > 0.f) || !isfinite(c.softmax_scale))
+        return fail(MFA_ERR_INVALID, "mfa_create: softmax_scale must be finite and > 0");
+    if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))
+        return fail(MFA_ERR_INVALID, "mfa_create: rms_eps must be finite and >= 0");
+
+    const int min_chunk = c.split_tokens > 0 ? c.split_tokens : kMinAutoSplit;
+    const int64_t max_chunks = ((int64_t)c.max_context + min_chunk - 1) / min_chunk;
+    const int64_t nparts = (int64_t)c.max_batch * max_chunks;
+    const int64_t bytes_o = nparts * mfa::kHeads * mfa::kHeadDim * 4;
+    const int64_t bytes_lse = nparts * mfa::kHeads * 4;
+    const int64_t bytes_c = (int64_t)mfa::kQprojSplit * c.max_batch * c.q_rank * 4;
+    const int64_t bytes_chat = (int64_t)c.max_batch * c.q_rank * 2;
+    if (max_chunks > (1 << 24) || nparts > (int64_t)1 << 31)
+        return fail(MFA_ERR_INVALID, "mfa_create: max_batch * max_context too large");
+
+    mfa_ctx* h = new (std::nothrow) mfa_ctx();
+    if (!h) return fail(MFA_ERR_NOMEM, "mfa_create: host allocation failed");
+    h->cfg = c;
+    h->max_chunks = (int)max_chunks;
+    hipError_t e = hipGetDevice(&h->device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e, "mfa_create: device query");
+    }
+    void* p[4] = {nullptr, nullptr, nullptr, nullptr};
+    const int64_t sizes[4] = {bytes_o, bytes_lse, bytes_c, bytes_chat};
+    for (int i = 0; i < 4; i++) {
+        e = hipMalloc(&p[i], (size_t)sizes[i]);
+        if (e != hipSuccess) {
+            for (int j = 0; j < i; j++) (void)hipFree(p[j]);
+            delete h;
+            (void)hipGetLastError();
+            return fail(MFA_ERR_NOMEM, "mfa_create: workspace allocation of %lld bytes failed: %s",
+                        (long long)sizes[i], hipGetErrorString(e));
+        }
+    }
+    h->part_o = (float*)p[0];
+    h->part_lse = (float*)p[1];
+    h->c_part = (float*)p[2];
+    h->chat = (uint16_t*)p[3];
+    h->magic = kMagic;
+    *out = h;
+    return MFA_OK;
+}
+
+int mfa_destroy(mfa_handle h) {
+    g_last_error[0] = 0;
+    if (!h) return MFA_OK;
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_destroy: not a live handle");
+    h->magic = kDead;
+    (void)hipFree(h->part_o);
+    (void)hipFree(h->part_lse);
+    (void)hipFree(h->c_part);
+    (void)hipFree(h->chat);
+    delete h;
+    return MFA_OK;
+}
+
+int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len) {
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_split_tokens: not a live handle");
+    if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;
+    return choose_split(h, batch, max_seq_len);
+}
+
+int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w, const void* w_qb,
+              void* q_out, int32_t batch, void* hip_stream) {
+    g_last_error[0] = 0;
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_qproj: not a live handle");
+    if (!x || !w_qa || !rms_w || !w_qb || !q_out)
+        return fail(MFA_ERR_INVALID, "mfa_qproj: null tensor pointer");
+    if (batch < 1 || batch > h->cfg.max_batch)
+        return fail(MFA_ERR_INVALID, "mfa_qproj: batch %d outside [1, %d]", batch, h->cfg.max_batch);
+    mfa::QprojArgs a;
+    a.x = (const uint16_t*)x;
+    a.w_qa = (const uint16_t*)w_qa;
+    a.rms_w = (const uint16_t*)rms_w;
+    a.w_qb = (const uint16_t*)w_qb;
+    a.q_out = (uint16_t*)q_out;
+    a.c_part = h->c_part;
+    a.chat = h->chat;
+    a.batch = batch;
+    a.hidden = h->cfg.hidden;
+    a.rank = h->cfg.q_rank;
+    a.nq = mfa::kHeads * mfa::kHeadDim;
+    a.ksplit = mfa::kQprojSplit;
+    a.eps = h->cfg.rms_eps;
+    hipError_t e = mfa::launch_qproj(a, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return hip_fail(e, "mfa_qproj: launch");
+    return MFA_OK;
+}
+
+static int check_kv(const mfa_ctx* h, const mfa_kv* kv, int32_t batch, const char* fn, int32_t* max_len) {
+    if (!kv) return fail(MFA_ERR_INVALID, "%s: null kv", fn);
+    if (!kv->k || !kv->v || !kv->seq_lens) return fail(MFA_ERR_INVALID, "%s: null k, v or seq_lens", fn);
+    const int32_t ml = kv->max_seq_len > 0 ? kv->max_seq_len : h->cfg.max_context;
+    if (kv->max_seq_len < 0 || ml > h->cfg.max_context)
+        return fail(MFA_ERR_INVALID, "%s: max_seq_len %d outside [0, max_context %d]", fn, kv->max_seq_len,
+                    h->cfg.max_context);
+    if (h->cfg.page_size) {
+        if (!kv->page_table) return fail(MFA_ERR_INVALID, "%s: paged handle needs a page_table", fn);
+        if (kv->pt_stride < (ml + mfa::kPage - 1) / mfa::kPage)
+            return fail(MFA_ERR_INVALID, "%s: pt_stride %d < ceil(max_seq_len/64) = %d", fn, kv->pt_stride,
+                        (ml + mfa::kPage - 1) / mfa::kPage);
+        if (kv->num_pages < 1) return fail(MFA_ERR_INVALID, "%s: num_pages must be >= 1", fn);
+    } else {
+        if (kv->page_table) return fail(MFA_ERR_INVALID, "%s: contiguous handle got a page_table", fn);
+        if (kv->kv_stride < ml)
+            return fail(MFA_ERR_INVALID, "%s: kv_stride %lld < max_seq_len %d", fn, (long long)kv->kv_stride, ml);
+    }
+    if (h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3) {
+        if (!(kv->k_scale > 0.f) || !isfinite(kv->k_scale) || !(kv->v_scale > 0.f) || !isfinite(kv->v_scale))
+            return fail(MFA_ERR_INVALID, "%s: FP8 scales must be finite and > 0 (k %g, v %g)", fn,
+                        (double)kv->k_scale, (double)kv->v_scale);
+    }
+    if (batch < 1 || batch > h->cfg.max_batch)
+        return fail(MFA_ERR_INVALID, "%s: batch %d outside [1, %d]", fn, batch, h->cfg.max_batch);
+    *max_len = ml;
+    return MFA_OK;
+}
+
+static mfa::KvView make_view(const mfa_ctx* h, const mfa_kv* kv, int32_t max_len) {
+    mfa::KvView v;
+    v.k = (const uint8_t*)kv->k;
+    v.v = (const uint8_t*)kv->v;
+    v.seq_lens = kv->seq_lens;
+    v.page_table = h->cfg.page_size ? kv->page_table : nullptr;
+    v.kv_stride = kv->kv_stride;
+    v.pt_stride = kv->pt_stride;
+    v.row_bytes = mfa::kHeadDim * (h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3 ? 1 : 2);
+    v.max_len = max_len;
+    return v;
+}
+
+int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out, int32_t batch,
+               void* hip_stream) {
+    g_last_error[0] = 0;
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_decode: not a live handle");
+    if (!q || !out) return fail(MFA_ERR_INVALID, "mfa_decode: null q or out");
+    int32_t max_len = 0;
+    int rc = check_kv(h, kv, batch, "mfa_decode", &max_len);
+    if (rc) return rc;
+    const bool fp8 = h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3;
+    mfa::AttnArgs a;
+    a.q = (const uint16_t*)q;
+    a.kv = make_view(h, kv, max_len);
+    a.out = (uint16_t*)out;
+    a.lse_out = lse_out;
+    a.part_o = h->part_o;
+    a.part_lse = h->part_lse;
+    a.chunk = choose_split(h, batch, max_len);
+    a.n_chunk = (max_len + a.chunk - 1) / a.chunk;
+    if (a.n_chunk < 1) a.n_chunk = 1;
+    if (a.n_chunk > h->max_chunks)
+        return fail(MFA_ERR_INVALID, "mfa_decode: %d chunks exceed the workspace (%d)", a.n_chunk, h->max_chunks);
+    const float log2e = 1.4426950408889634f;
+    a.score_scale = h->cfg.softmax_scale * (fp8 ? kv->k_scale : 1.0f) * log2e;
+    a.v_scale = fp8 ? kv->v_scale : 1.0f;
+    hipError_t e = mfa::launch_attention(a, fp8, h->cfg.page_size != 0, batch, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return hip_fail(e, "mfa_decode: launch");
+    return MFA_OK;
+}
+
+int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, void* v_dst,
+                        void* hip_stream) {
+    g_last_error[0] = 0;
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_debug_gather_kv: not a live handle");
+    if (!k_dst || !v_dst) return fail(MFA_ERR_INVALID, "mfa_debug_gather_kv: null destination");
+    int32_t max_len = 0;
+    int rc = check_kv(h, kv, h->cfg.max_batch, "mfa_debug_gather_kv", &max_len);
+    if (rc) return rc;
+    if (b < 0 || b >= h->cfg.max_batch)
+        return fail(MFA_ERR_INVALID, "mfa_debug_gather_kv: sequence %d outside [0, %d)", b, h->cfg.max_batch);
+    hipError_t e = mfa::launch_gather(make_view(h, kv, max_len), h->cfg.page_size != 0, b, max_len, k_dst, v_dst,
+                                      (hipStream_t)hip_stream);
+    if (e != hipSuccess) return hip_fail(e, "mfa_debug_gather_kv: launch");
+    return MFA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// mfa_device.h -- device-side helpers shared by the MFA kernels (gfx950).
+//
+// Vector types for the CDNA4 matrix cores, FP8 E4M3 -> bf16 conversion in
+// registers, and the KV-cache address generation used by both the attention
+// kernel and the debug gather (so that the two follow one code path).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeads = 64;      // query heads sharing one K/V head
+constexpr int kHeadDim = 256;   // head dimension of Q, K and V
+constexpr int kPage = 64;       // tokens per cache page
+constexpr int kStep = 64;       // tokens per attention step (one page)
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <typename T, typename S>
+__device__ __forceinline__ T bitcast(const S& s) {
+    static_assert(sizeof(T) == sizeof(S), "size mismatch");
+    return __builtin_bit_cast(T, s);
+}
+
+// 16x16x32 bf16 MFMA, fp32 accumulate. Lane l holds A[l%16][8*(l/16)+j],
+// B[8*(l/16)+j][l%16] (j = 0..7) and D[4*(l/16)+i][l%16] (i = 0..3).
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Four E4M3FN codes (one dword, byte 0 first) -> four bf16, exactly: every
+// E4M3 value is a bf16 value. Scale 1.0 leaves values unchanged.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+    bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+}
+
+// Eight E4M3 codes (two dwords) -> a bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    u32x2 a = e4m3x4_to_bf16x4(w0);
+    u32x2 b = e4m3x4_to_bf16x4(w1);
+    return bitcast<bf16x8>(u32x4{a.x, a.y, b.x, b.y});
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};  // round to nearest even
+    return bitcast<uint32_t>(v);
+}
+
+__device__ __forceinline__ float bf16_round(float a) {
+    return (float)(__bf16)a;
+}
+
+// KV cache view used on the device.
+struct KvView {
+    const uint8_t* k;
+    const uint8_t* v;
+    const int32_t* seq_lens;
+    const int32_t* page_table;  // nullptr: contiguous
+    int64_t kv_stride;          // contiguous: token slots per sequence
+    int32_t pt_stride;
+    int32_t row_bytes;          // 256 * element size
+    int32_t max_len;            // launch bound on sequence lengths
+};
+
+// Length of sequence b as the kernels use it: seq_lens[b] clamped to
+// [0, max_len], so a bad length can never address rows past the launch bound.
+__device__ __forceinline__ int seq_len(const KvView& kv, int b) {
+    return min(max(kv.seq_lens[b], 0), kv.max_len);
+}
+
+// Row index of token t of sequence b. For a paged cache the page of token t
+// is page_table[b][t / 64] and the row inside it t % 64.
+template <bool PAGED>
+__device__ __forceinline__ int64_t kv_row(const KvView& kv, int b, int t) {
+    if constexpr (PAGED) {
+        int32_t page = kv.page_table[(int64_t)b * kv.pt_stride + (t >> 6)];
+        return (int64_t)page * kPage + (t & (kPage - 1));
+    } else {
+        return (int64_t)b * kv.kv_stride + t;
+    }
+}
+
+// Row index of the first token of the 64-token step starting at t0 (a
+// multiple of 64). All tokens t0..t0+63 are rows base+0..base+63.
+template <bool PAGED>
+__device__ __forceinline__ int64_t kv_step_base(const KvView& kv, int b, int t0) {
+    return kv_row<PAGED>(kv, b, t0);
+}
+
+}  // namespace mfa

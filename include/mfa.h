@@ -1,0 +1,154 @@
+/*
+ * mfa.h -- C ABI of the MI355X (gfx950) decode step of Multi-Matrix
+ * Factorization Attention (MFA).
+ *
+ * One MFA layer, one decode step (one new query token per sequence):
+ *   - a low-rank query path: hidden 7168 -> 2048-wide bottleneck ->
+ *     64 query heads x 256 ("Step-3 is Large yet Affordable", Key points:
+ *     hidden size, the 2048-dim query bottleneck, 64 query heads);
+ *   - attention of all 64 heads against ONE shared key head and ONE shared
+ *     value head of dimension 256 held in a KV cache (same page, Key points);
+ *   - the cache in bf16 or FP8 E4M3 (the FP8 deployment in the same Key
+ *     points), contiguous or in pages of 64 tokens (PagedAttention, cited by
+ *     title on the Step-3 references);
+ *   - long contexts split into chunks merged by the log-sum-exp identity
+ *     (Flash-Decoding, cited by title on the DeepSeek-V4 references).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers unless marked (host). The caller
+ *     allocates and owns every tensor; the library never frees them.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
+ *     stream) and returns without synchronising. Nothing reads device
+ *     memory on the host.
+ *   - Arguments are checked on the host before any launch; on error the call
+ *     enqueues nothing, returns a negative MFA_ERR_* status and records a
+ *     message readable with mfa_last_error() (thread-local).
+ *   - A device fault (for example a page index outside the pool) is not
+ *     detected; it surfaces at the caller's next synchronisation.
+ *   - A handle may be used by one stream at a time: calls that overlap on
+ *     different streams share the handle's workspace and race.
+ *   - Layouts are row-major, innermost index last. bf16 is IEEE binary32's
+ *     upper half; FP8 is OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN).
+ */
+#ifndef MFA_H
+#define MFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mfa_status {
+    MFA_OK = 0,
+    MFA_ERR_INVALID = -1,     /* bad argument: null pointer, size out of range, bad handle */
+    MFA_ERR_UNSUPPORTED = -2, /* valid but not implemented: heads != 64, head_dim != 256, ... */
+    MFA_ERR_NOMEM = -3,       /* workspace allocation failed */
+    MFA_ERR_HIP = -4          /* a HIP runtime call failed (message has the HIP error) */
+};
+
+enum mfa_kv_dtype {
+    MFA_DTYPE_BF16 = 0,
+    MFA_DTYPE_FP8_E4M3 = 1
+};
+
+typedef struct mfa_ctx* mfa_handle;
+
+/* Layer configuration (host struct, copied by mfa_create). */
+typedef struct {
+    int32_t hidden;        /* model width, 7168; multiple of 512 */
+    int32_t q_rank;        /* query bottleneck, 2048; multiple of 64 */
+    int32_t num_heads;     /* query heads, must be 64 */
+    int32_t head_dim;      /* must be 256 */
+    int32_t kv_dtype;      /* enum mfa_kv_dtype */
+    int32_t page_size;     /* 0 = contiguous cache; otherwise must be 64 */
+    int32_t max_batch;     /* largest batch any call will pass, >= 1 */
+    int32_t max_context;   /* largest sequence length any call will pass, >= 1 */
+    int32_t split_tokens;  /* split-K chunk in tokens, multiple of 64; 0 = chosen per call */
+    float rms_eps;         /* RMSNorm epsilon (1e-6), >= 0 */
+    float softmax_scale;   /* score scale (1/16 = 1/sqrt(256)), finite and > 0 */
+} mfa_config;
+
+/* KV cache of one layer for one call (host struct describing device buffers).
+ *   contiguous (page_size 0): k, v are [batch][kv_stride][256]; token t of
+ *     sequence b is row b * kv_stride + t.
+ *   paged (page_size 64): k, v are pools [num_pages][64][256] sharing page
+ *     numbers; token t of sequence b is row t % 64 of page
+ *     page_table[b * pt_stride + t / 64].
+ * Element type: bf16 or E4M3 per the handle's kv_dtype. An FP8 element's
+ * value is decode(code) * k_scale (keys) or * v_scale (values). Only rows
+ * t < seq_lens[b] are read. */
+typedef struct {
+    const void* k;
+    const void* v;
+    float k_scale;              /* FP8 only: finite, > 0. Ignored for bf16 */
+    float v_scale;              /* FP8 only: finite, > 0. Ignored for bf16 */
+    const int32_t* seq_lens;    /* [batch], 0 <= L_b <= max_seq_len (values outside are clamped) */
+    const int32_t* page_table;  /* [batch][pt_stride] int32, or NULL when contiguous */
+    int32_t pt_stride;          /* paged: entries per page-table row, >= ceil(max_seq_len/64) */
+    int32_t num_pages;          /* paged: pool size in pages (documentation; not checked on device) */
+    int64_t kv_stride;          /* contiguous: token slots per sequence, >= max_seq_len */
+    int32_t max_seq_len;        /* (host) upper bound of seq_lens in this call, sizes the
+                                   launch; 0 = the handle's max_context */
+} mfa_kv;
+
+/* Create a handle for one layer shape. Validates `cfg` (host pointer) and
+ * allocates the split-K workspace on the current device:
+ *   max_batch * ceil(max_context / 64) * 64 * (256 + 1) * 4 bytes (partial
+ *   outputs and log-sum-exps) plus the Q-projection scratch
+ *   max_batch * q_rank * 4 bytes * 8.
+ * On success stores the handle in *out (host pointer) and returns MFA_OK. */
+int mfa_create(const mfa_config* cfg, mfa_handle* out);
+
+/* Query projection with RMSNorm on the bottleneck (Step-3 Key points: the
+ * 2048-dim low-rank query bottleneck; the norm's placement is this
+ * library's reading, the pages do not state it):
+ *   c    = x . w_qa                         x [batch][hidden] bf16,
+ *                                           w_qa [hidden][q_rank] bf16
+ *   chat = c * rsqrt(mean(c^2) + rms_eps) * rms_w      rms_w [q_rank] bf16
+ *   q    = chat . w_qb                      w_qb [q_rank][64*256] bf16
+ * q_out is [batch][64][256] bf16 (= [batch][16384]); c accumulates in fp32,
+ * chat is rounded to bf16 before the second product.
+ * 1 <= batch <= max_batch. */
+int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
+              const void* w_qb, void* q_out, int32_t batch, void* hip_stream);
+
+/* Decode attention of one step:
+ *   s_bht  = softmax_scale * <q[b][h][:], K_b[t][:]>      for t < L_b
+ *   out[b][h][:] = sum_t softmax_t(s_bh) * V_b[t][:]       bf16
+ *   lse_out[b][h] = log(sum_t exp(s_bht))                  fp32, natural log
+ * q [batch][64][256] bf16; out [batch][64][256] bf16; lse_out [batch][64]
+ * fp32 or NULL. L_b = 0 gives out = 0 and lse = -inf.
+ * The KV range of each sequence is cut into chunks of split_tokens tokens
+ * (or a per-call choice when split_tokens is 0); chunk partials go to the
+ * handle's workspace and are merged by the log-sum-exp identity. The result
+ * depends only on the logical K/V values and the chunking, not on the cache
+ * layout: paged and contiguous caches holding the same rows give bitwise
+ * equal outputs. 1 <= batch <= max_batch. */
+int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out,
+               int32_t batch, void* hip_stream);
+
+/* The split-K chunk (tokens) mfa_decode uses for this batch and kv->max_seq_len. */
+int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len);
+
+/* Test support: copy the logical K and V rows t < L_b of sequence b into
+ * contiguous device buffers k_dst, v_dst ([max_seq_len][256] elements of the
+ * cache type) with the same address generation mfa_decode uses. */
+int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, void* v_dst,
+                        void* hip_stream);
+
+/* Release the handle and its workspace. NULL is accepted. The caller must
+ * ensure no enqueued call that uses the handle is still running. */
+int mfa_destroy(mfa_handle h);
+
+/* Static text for a status code. */
+const char* mfa_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* mfa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFA_H */

@@ -1,0 +1,201 @@
+"""GPU parity of mfa_decode against the fp64 oracle, through the C ABI.
+
+Metric (one reading of "max relative error 1e-2"): for every (sequence,
+head) row, ||o_gpu - o_ref||_inf / ||o_ref||_inf; the test takes the max over
+rows. Element-wise relative error is meaningless on near-zero entries of a
+softmax average. The log-sum-exp is compared in absolute terms.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2        # row-wise normwise relative error of the bf16 output
+LSE_TOL = 2e-3    # absolute, natural log
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _mfa():
+    import decode_attention_mfa_amd as m
+    from decode_attention_mfa_amd import harness
+    return m, harness
+
+
+def row_err(o_gpu, o_ref, lens=None):
+    err = np.abs(o_gpu - o_ref).max(axis=-1) / np.maximum(np.abs(o_ref).max(axis=-1), 1e-30)
+    if lens is not None:
+        err = err[np.asarray(lens) > 0]
+    return float(err.max()) if err.size else 0.0
+
+
+def check_parity(case, split_tokens=None, label=""):
+    m, hz = _mfa()
+    _say(f"[parity] {label or case.name}: B={case.batch} kv={case.kv_dtype} paged={case.paged} "
+         f"L=[{case.seq_lens.min()},{case.seq_lens.max()}] split={split_tokens}")
+    dc = hz.to_device(case)
+    out, lse, _ = hz.run_case(dc, split_tokens=split_tokens)
+    o_ref, lse_ref = oracle.case_attention(case)
+    o = hz.bf16_to_f64(out)
+    lse_gpu = lse.cpu().numpy().astype(np.float64)
+    nz = case.seq_lens > 0
+    e = row_err(o, o_ref, case.seq_lens)
+    el = float(np.abs(lse_gpu[nz] - lse_ref[nz]).max()) if nz.any() else 0.0
+    _say(f"    row-rel err {e:.3e}  lse abs err {el:.3e}")
+    assert e <= TOL, e
+    assert el <= LSE_TOL, el
+    if (~nz).any():
+        assert np.all(o[~nz] == 0) and np.all(np.isneginf(lse_gpu[~nz]))
+    return out, lse
+
+
+def test_tiny_config():
+    check_parity(synth.config_case(1), label="tiny B=1 L=256 bf16")
+
+
+@pytest.mark.parametrize("split", [0, 64, 192, 1024, 4096])
+def test_fp8_contiguous_splits(split):
+    check_parity(synth.config_case(3, batch=3, scale_len=0.5), split_tokens=split,
+                 label=f"fp8 contiguous B=3 L=2048 split={split}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_ragged_tails(kv):
+    L = [1, 63, 64, 65, 127, 129, 1000, 2049]
+    case = synth.make_case("ragged", len(L), L, kv, seed=77, kv_slack=5)
+    check_parity(case, split_tokens=256, label=f"ragged tails {kv}")
+    check_parity(case, split_tokens=0, label=f"ragged tails {kv} auto split")
+
+
+def test_empty_sequences():
+    case = synth.make_case("empty", 4, [0, 5, 0, 300], "fp8", seed=78)
+    check_parity(case, split_tokens=128, label="empty sequences")
+
+
+def test_peaky_scores():
+    """Q scaled by 8: logits with std ~8 exercise the running-max rescale."""
+    case = synth.config_case(3, batch=2, scale_len=0.25, q_std=8.0)
+    check_parity(case, split_tokens=256, label="peaky fp8")
+    case = synth.config_case(5, batch=2, scale_len=1 / 32, q_std=8.0)
+    check_parity(case, label="peaky bf16")
+
+
+def test_paged_ragged_reduced():
+    check_parity(synth.config_case(4, batch=24, scale_len=1 / 16), label="paged ragged B=24")
+    check_parity(synth.config_case(4, batch=24, scale_len=1 / 16), split_tokens=128,
+                 label="paged ragged B=24 split=128")
+
+
+def test_long_splitk_reduced():
+    check_parity(synth.config_case(5, batch=4, scale_len=1 / 16), label="long split-K B=4 L=2K/4K")
+
+
+def test_paged_equals_contiguous_bitwise():
+    """Same logical rows via a permuted page table and via a contiguous cache,
+    same chunking: bitwise identical outputs."""
+    m, hz = _mfa()
+    for kv in ("fp8", "bf16"):
+        pc = synth.make_case("p", 6, [1, 64, 65, 700, 1500, 333], kv, seed=79, paged=True,
+                             max_context=1536)
+        maxL = int(pc.seq_lens.max())
+        kc = np.zeros((pc.batch, maxL, 256), pc.k.dtype)
+        vc = np.zeros_like(kc)
+        for b in range(pc.batch):
+            t = np.arange(int(pc.seq_lens[b]))
+            pages = pc.page_table[b, t // 64]
+            kc[b, :len(t)] = pc.k[pages, t % 64]
+            vc[b, :len(t)] = pc.v[pages, t % 64]
+        cc = synth.Case(name="c", batch=pc.batch, kv_dtype=kv, seq_lens=pc.seq_lens, k=kc, v=vc,
+                        q=pc.q, k_scale=pc.k_scale, v_scale=pc.v_scale)
+        for split in (128, 512):
+            _say(f"[bitwise] paged vs contiguous {kv} split={split}")
+            o1, l1, _ = hz.run_case(hz.to_device(pc), split_tokens=split)
+            o2, l2, _ = hz.run_case(hz.to_device(cc), split_tokens=split)
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_debug_gather_bit_exact():
+    m, hz = _mfa()
+    for kv in ("fp8", "bf16"):
+        pc = synth.make_case("g", 5, [1, 63, 64, 200, 511], kv, seed=80, paged=True)
+        dc = hz.to_device(pc)
+        h = hz.create_handle(dc)
+        try:
+            for b in range(pc.batch):
+                _say(f"[gather] {kv} b={b}")
+                kd = torch.zeros((dc.max_len, 256), dtype=dc.k.dtype, device="cuda")
+                vd = torch.zeros_like(kd)
+                m.mfa_debug_gather_kv(h, dc.kv(), b, kd, vd)
+                torch.cuda.synchronize()
+                kr, vr = oracle.gather_kv(pc.k, pc.v, pc.seq_lens, b, page_table=pc.page_table)
+                n = int(pc.seq_lens[b])
+                kg = kd[:n].cpu().numpy().view(kr.dtype)
+                vg = vd[:n].cpu().numpy().view(vr.dtype)
+                assert np.array_equal(kg, kr) and np.array_equal(vg, vr)
+        finally:
+            m.mfa_destroy(h)
+
+
+def test_deterministic_run_twice():
+    m, hz = _mfa()
+    case = synth.config_case(4, batch=16, scale_len=1 / 16)
+    dc = hz.to_device(case)
+    _say("[determinism] paged fp8 B=16, two runs")
+    o1, l1, _ = hz.run_case(dc, split_tokens=128)
+    o2, l2, _ = hz.run_case(dc, split_tokens=128)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_lse_null_is_allowed():
+    m, hz = _mfa()
+    case = synth.config_case(1)
+    dc = hz.to_device(case)
+    h = hz.create_handle(dc)
+    try:
+        out = torch.empty((1, 64, 256), dtype=torch.int16, device="cuda")
+        m.mfa_decode(h, dc.q, dc.kv(), out, None, 1)
+        torch.cuda.synchronize()
+        o_ref, _ = oracle.case_attention(case)
+        assert row_err(hz.bf16_to_f64(out), o_ref) <= TOL
+    finally:
+        m.mfa_destroy(h)
+
+
+def test_host_errors_enqueue_nothing():
+    m, hz = _mfa()
+    case = synth.config_case(1)
+    dc = hz.to_device(case)
+    h = hz.create_handle(dc)
+    try:
+        out = torch.full((1, 64, 256), 7, dtype=torch.int16, device="cuda")
+        with pytest.raises(m.MfaError) as ei:
+            m.mfa_decode(h, dc.q, dc.kv(), out, None, 2)          # batch > max_batch
+        assert ei.value.status == m.MFA_ERR_INVALID
+        with pytest.raises(m.MfaError):
+            m.mfa_decode(h, dc.q, dc.kv(max_seq_len=100000), out, None, 1)
+        with pytest.raises(m.MfaError):
+            m.mfa_decode(h, None, dc.kv(), out, None, 1)
+        torch.cuda.synchronize()
+        assert torch.all(out == 7)
+    finally:
+        m.mfa_destroy(h)
+    fp8 = synth.make_case("s", 1, 64, "fp8", seed=81)
+    dc = hz.to_device(fp8)
+    h = hz.create_handle(dc)
+    try:
+        kv = dc.kv()
+        kv.k_scale = float("nan")
+        with pytest.raises(m.MfaError) as ei:
+            m.mfa_decode(h, dc.q, kv, torch.empty(1, 64, 256, dtype=torch.int16, device="cuda"), None, 1)
+        assert "scale" in str(ei.value)
+    finally:
+        m.mfa_destroy(h)
