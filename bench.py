@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the MFA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload fp8_contig]
+
+A step is one pass of the hot path over one batch: the decode attention
+(chunked scores, online softmax, P.V, log-sum-exp merge) and, for the
+full-layer workload, the Q projection with RMSNorm before it. Inputs are
+seeded synthetic tensors already resident in HBM; several copies are rotated
+so that consecutive steps do not find their KV cache in the 256 MB MALL.
+
+Prints one JSON line: tokens/s per layer (batch / step time), the attention
+kernel's achieved algorithmic HBM bandwidth against 8 TB/s (timed with HIP
+events recorded by the library around each launch, on the launch stream),
+and the fp64 CPU oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MFA decode tokens/s per layer (1 GPU) + achieved HBM GB/s vs roofline"
+HBM_PEAK_GBPS = 8000.0
+WORKLOADS = {"tiny": 1, "full_layer": 2, "fp8_contig": 3, "paged_ragged": 4, "long_splitk": 5}
+DESCRIPTION = {
+    "tiny": "B=1, L=256, bf16 KV, contiguous, decode only",
+    "full_layer": "B=32, L=4096, bf16 KV, contiguous, Q projection 7168->2048 (RMSNorm)->64x256 + decode",
+    "fp8_contig": "B=128, L=4096, FP8-E4M3 KV (per-tensor scales), contiguous, decode only",
+    "paged_ragged": "B=384, L~U[1024,8192], FP8-E4M3 KV, 64-token pages, permuted page table, decode only",
+    "long_splitk": "B=8, L=32768 x4 + 65536 x4, bf16 KV, split-K 512-token chunks, decode only",
+}
+ATTN_SOURCES = ("decode_attention_mfa_amd/csrc/mfa_attn.hip", "decode_attention_mfa_amd/csrc/mfa_device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case):
+    """(attention-kernel bytes, whole-step bytes) the method must move.
+    Attention: every cached K and V row t < L_b, Q, the lengths and (paged)
+    the page-table entries it reads. Step: that plus the bf16 output and, for
+    the full layer, x, gamma and both projection weights."""
+    import numpy as np
+    B = case.batch
+    kv = case.kv_bytes_read()
+    q = B * 64 * 256 * 2
+    o = B * 64 * 256 * 2
+    meta = B * 4
+    if case.paged:
+        meta += int(((case.seq_lens.astype(np.int64) + 63) // 64).sum()) * 4
+    attn = kv + q + meta
+    step = attn + o
+    if case.x is not None:
+        step += case.x.nbytes + case.w_qa.nbytes + case.w_qb.nbytes + case.gamma.nbytes
+        attn -= q          # Q is produced on the device, not an input of the step
+        step -= q
+    return attn, step
+
+
+def sample_case(case, n):
+    """The first n sequences of a workload (same cache pool when paged)."""
+    import copy
+    s = copy.copy(case)
+    s.batch = n
+    s.seq_lens = case.seq_lens[:n]
+    if case.q is not None:
+        s.q = case.q[:n]
+    if case.x is not None:
+        s.x = case.x[:n]
+    if case.paged:
+        s.page_table = case.page_table[:n]
+    else:
+        s.k = case.k[:n]
+        s.v = case.v[:n]
+    return s
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle, as it stands, on the first n sequences; n chosen from
+    a one-sequence probe so that the run takes about budget_s seconds."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.case_attention(sample_case(case, 1))
+    t1 = time.perf_counter() - t0
+    n = max(1, min(case.batch, int(budget_s / max(t1, 1e-3))))
+    s = sample_case(case, n)
+    t0 = time.perf_counter()
+    oracle.case_attention(s)
+    dt = time.perf_counter() - t0
+    what = "attention" if case.x is None else "Q projection + attention"
+    return {"value": n / dt, "unit": "tokens/s/layer", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{what} of the first {n} of {case.batch} sequences, fp64, {dt:.1f} s"}
+
+
+def load_traffic(workload: str, sha: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("source_sha") != sha:
+        return None
+    return float(e["traffic_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fp8_contig", choices=sorted(WORKLOADS))
+    ap.add_argument("--split", type=int, default=None, help="override the split-K chunk (tokens)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget; 0 skips it")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device copy of known size (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the MFA decode path has no multi-GPU mode here)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return
+
+    import decode_attention_mfa_amd as mfa
+    from decode_attention_mfa_amd import harness
+    import synth
+
+    wl = args.workload
+    log(f"[bench] generating workload {wl}: {DESCRIPTION[wl]}")
+    t0 = time.perf_counter()
+    case = synth.config_case(WORKLOADS[wl])
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f} s")
+    attn_bytes, step_bytes = algorithmic_bytes(case)
+
+    dc = harness.to_device(case)
+    # rotate copies of the per-step inputs so that no step finds them in the MALL
+    nrot = max(2, min(8, math.ceil(768e6 / max(step_bytes, 1)) + 1))
+    if step_bytes * nrot > 6e9:
+        nrot = 2
+    sets = [dc]
+    for _ in range(nrot - 1):
+        c = harness.DeviceCase(**{f: getattr(dc, f) for f in dc.__dataclass_fields__})
+        c.k, c.v = dc.k.clone(), dc.v.clone()
+        if dc.q is not None:
+            c.q = dc.q.clone()
+        if dc.x is not None:
+            c.x, c.w_qa, c.w_qb = dc.x.clone(), dc.w_qa.clone(), dc.w_qb.clone()
+        sets.append(c)
+    cold = nrot * step_bytes > 512e6
+
+    h = harness.create_handle(dc, split_tokens=args.split)
+    split = mfa.mfa_split_tokens(h, dc.batch, dc.max_len)
+    stream = torch.cuda.Stream()
+    outs = [harness.alloc_outputs(dc) for _ in range(nrot)]
+    qbufs = [torch.empty((dc.batch, 64, 256), dtype=torch.int16, device="cuda") for _ in range(nrot)]
+
+    def step(i):
+        s = sets[i % nrot]
+        o, l = outs[i % nrot]
+        q = s.q
+        if s.q is None:
+            q = qbufs[i % nrot]
+            mfa.mfa_qproj(h, s.x, s.w_qa, s.gamma, s.w_qb, q, s.batch, stream)
+        mfa.mfa_decode(h, q, s.kv(), o, l, s.batch, stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        mfa.mfa_profile_enable(h, True)
+        mfa.mfa_profile_read(h)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        prof = mfa.mfa_profile_read(h)
+        mfa.mfa_profile_enable(h, False)
+    mfa.mfa_destroy(h)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = dc.batch / (ms_per_step / 1e3)
+    n_attn, ms_attn = prof["attention"]
+    attn_ms = ms_attn / max(n_attn, 1)
+    achieved = attn_bytes / (attn_ms / 1e3) / 1e9
+    sha = attn_source_sha()
+    traffic = load_traffic(wl, sha)
+    kernels = {k: {"launches": n, "avg_us": round(ms * 1e3 / n, 2)} for k, (n, ms) in prof.items() if n}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s/layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": f"synthetic: seeded N(0,1) (numpy PCG64, seed {case.seed}), FP8 codes by RNE with "
+                "per-tensor amax scales",
+        "config": {"workload": wl, "description": DESCRIPTION[wl], "batch": case.batch,
+                   "context_min": int(case.seq_lens.min()), "context_max": int(case.seq_lens.max()),
+                   "kv_dtype": "fp8_e4m3" if case.kv_dtype == "fp8" else "bf16",
+                   "layout": "paged64" if case.paged else "contiguous", "split_tokens": split,
+                   "input_sets_rotated": nrot, "mall": "cold" if cold else "warm"},
+        "step_hbm_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "mfa_attn_split_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": attn_bytes,
+                     "avg_launch_us": round(attn_ms * 1e3, 2), "source_sha": sha},
+        "kernels": kernels,
+    }
+    if args.cpu_seconds > 0:
+        log("[bench] timing the fp64 CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

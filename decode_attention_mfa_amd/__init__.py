@@ -13,7 +13,8 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmfa.so")
+# MFA_LIBRARY may name another build of the same library (for A/B timing)
+LIB_PATH = os.environ.get("MFA_LIBRARY") or os.path.join(_PKG, "libmfa.so")
 
 MFA_OK = 0
 MFA_ERR_INVALID = -1
@@ -22,6 +23,7 @@ MFA_ERR_NOMEM = -3
 MFA_ERR_HIP = -4
 MFA_DTYPE_BF16 = 0
 MFA_DTYPE_FP8_E4M3 = 1
+KERNEL_KINDS = ("attention", "combine", "qproj_down", "rmsnorm", "qproj_up")
 
 
 class MfaError(RuntimeError):
@@ -64,6 +66,10 @@ def _load_lib():
     lib.mfa_split_tokens.restype = I32
     lib.mfa_debug_gather_kv.argtypes = [P, ctypes.POINTER(mfa_kv), I32, P, P, P]
     lib.mfa_debug_gather_kv.restype = ctypes.c_int
+    lib.mfa_profile_enable.argtypes = [P, ctypes.c_int]
+    lib.mfa_profile_enable.restype = ctypes.c_int
+    lib.mfa_profile_read.argtypes = [P, P, P]
+    lib.mfa_profile_read.restype = ctypes.c_int
     lib.mfa_destroy.argtypes = [P]
     lib.mfa_destroy.restype = ctypes.c_int
     lib.mfa_status_string.argtypes = [ctypes.c_int]
@@ -158,6 +164,19 @@ def mfa_split_tokens(h: int, batch: int, max_seq_len: int = 0) -> int:
 def mfa_debug_gather_kv(h: int, kv: mfa_kv, b: int, k_dst, v_dst, stream=None) -> None:
     _check(lib.mfa_debug_gather_kv(h, ctypes.byref(kv), b, _ptr(k_dst), _ptr(v_dst),
                                    _stream(stream)), "mfa_debug_gather_kv")
+
+
+def mfa_profile_enable(h: int, enable: bool = True) -> None:
+    _check(lib.mfa_profile_enable(h, int(bool(enable))), "mfa_profile_enable")
+
+
+def mfa_profile_read(h: int) -> dict:
+    """{kind: (launches, total_ms)} for the launches since the last read."""
+    n = (ctypes.c_int32 * len(KERNEL_KINDS))()
+    ms = (ctypes.c_double * len(KERNEL_KINDS))()
+    _check(lib.mfa_profile_read(h, ctypes.cast(n, ctypes.c_void_p), ctypes.cast(ms, ctypes.c_void_p)),
+           "mfa_profile_read")
+    return {k: (int(n[i]), float(ms[i])) for i, k in enumerate(KERNEL_KINDS)}
 
 
 def mfa_destroy(h: Optional[int]) -> None:

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <new>
+#include <vector>
 
 #include "mfa.h"
 #include "mfa_internal.h"
@@ -34,8 +35,19 @@ constexpr int kMaxAutoSplit = 2048;
 
 }  // namespace
 
+// Optional per-kernel timing: a ring of hipEvent pairs recorded around each
+// launch on the call's stream.
+struct Profiler {
+    static constexpr int kCap = 4096;
+    bool on = false;
+    std::vector<hipEvent_t> ev;   // 2 * kCap events, created on enable
+    std::vector<int> kind;        // kind of each recorded pair, -1 = empty
+    int next = 0;
+};
+
 struct mfa_ctx {
     uint32_t magic;
+    Profiler prof;
     mfa_config cfg;
     int device;
     int num_cu;
@@ -47,6 +59,30 @@ struct mfa_ctx {
 };
 
 static bool valid_handle(mfa_handle h) { return h != nullptr && h->magic == kMagic; }
+
+// Launch `fn` on `st`, bracketed by a profiling event pair when enabled.
+template <typename F>
+static hipError_t timed_launch(mfa_ctx* h, int kind, hipStream_t st, F&& fn) {
+    Profiler& p = h->prof;
+    if (!p.on) return fn();
+    const int i = p.next;
+    p.next = (p.next + 1) % Profiler::kCap;
+    hipError_t e = hipEventRecord(p.ev[2 * i], st);
+    if (e != hipSuccess) return e;
+    e = fn();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(p.ev[2 * i + 1], st);
+    if (e == hipSuccess) p.kind[i] = kind;
+    return e;
+}
+
+static void profiler_release(Profiler& p) {
+    for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+    p.ev.clear();
+    p.kind.clear();
+    p.on = false;
+    p.next = 0;
+}
 
 static int round_up(int64_t a, int64_t m) { return (int)(((a + m - 1) / m) * m); }
 
@@ -151,6 +187,7 @@ int mfa_destroy(mfa_handle h) {
     if (!h) return MFA_OK;
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_destroy: not a live handle");
     h->magic = kDead;
+    profiler_release(h->prof);
     (void)hipFree(h->part_o);
     (void)hipFree(h->part_lse);
     (void)hipFree(h->c_part);
@@ -187,7 +224,10 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w, 
     a.nq = mfa::kHeads * mfa::kHeadDim;
     a.ksplit = mfa::kQprojSplit;
     a.eps = h->cfg.rms_eps;
-    hipError_t e = mfa::launch_qproj(a, (hipStream_t)hip_stream);
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e = timed_launch(h, MFA_KERNEL_QPROJ_DOWN, st, [&] { return mfa::launch_qproj_down(a, st); });
+    if (e == hipSuccess) e = timed_launch(h, MFA_KERNEL_RMSNORM, st, [&] { return mfa::launch_rmsnorm(a, st); });
+    if (e == hipSuccess) e = timed_launch(h, MFA_KERNEL_QPROJ_UP, st, [&] { return mfa::launch_qproj_up(a, st); });
     if (e != hipSuccess) return hip_fail(e, "mfa_qproj: launch");
     return MFA_OK;
 }
@@ -258,7 +298,12 @@ int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* 
     const float log2e = 1.4426950408889634f;
     a.score_scale = h->cfg.softmax_scale * (fp8 ? kv->k_scale : 1.0f) * log2e;
     a.v_scale = fp8 ? kv->v_scale : 1.0f;
-    hipError_t e = mfa::launch_attention(a, fp8, h->cfg.page_size != 0, batch, (hipStream_t)hip_stream);
+    hipStream_t st = (hipStream_t)hip_stream;
+    const bool paged = h->cfg.page_size != 0;
+    hipError_t e = timed_launch(h, MFA_KERNEL_ATTENTION, st,
+                                [&] { return mfa::launch_attn_split(a, fp8, paged, batch, st); });
+    if (e == hipSuccess && a.n_chunk > 1)
+        e = timed_launch(h, MFA_KERNEL_COMBINE, st, [&] { return mfa::launch_combine(a, batch, st); });
     if (e != hipSuccess) return hip_fail(e, "mfa_decode: launch");
     return MFA_OK;
 }
@@ -276,6 +321,53 @@ int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, 
     hipError_t e = mfa::launch_gather(make_view(h, kv, max_len), h->cfg.page_size != 0, b, max_len, k_dst, v_dst,
                                       (hipStream_t)hip_stream);
     if (e != hipSuccess) return hip_fail(e, "mfa_debug_gather_kv: launch");
+    return MFA_OK;
+}
+
+int mfa_profile_enable(mfa_handle h, int enable) {
+    g_last_error[0] = 0;
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_profile_enable: not a live handle");
+    Profiler& p = h->prof;
+    if (!enable) {
+        profiler_release(p);
+        return MFA_OK;
+    }
+    if (p.on) return MFA_OK;
+    p.ev.assign(2 * Profiler::kCap, nullptr);
+    p.kind.assign(Profiler::kCap, -1);
+    for (auto& e : p.ev) {
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            profiler_release(p);
+            return hip_fail(r, "mfa_profile_enable: hipEventCreate");
+        }
+    }
+    p.next = 0;
+    p.on = true;
+    return MFA_OK;
+}
+
+int mfa_profile_read(mfa_handle h, int32_t* launches, double* total_ms) {
+    g_last_error[0] = 0;
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_profile_read: not a live handle");
+    if (!launches || !total_ms) return fail(MFA_ERR_INVALID, "mfa_profile_read: null output");
+    for (int k = 0; k < MFA_KERNEL_KINDS; k++) {
+        launches[k] = 0;
+        total_ms[k] = 0.0;
+    }
+    Profiler& p = h->prof;
+    if (!p.on) return MFA_OK;
+    for (int i = 0; i < Profiler::kCap; i++) {
+        if (p.kind[i] < 0) continue;
+        hipError_t r = hipEventSynchronize(p.ev[2 * i + 1]);
+        float ms = 0.f;
+        if (r == hipSuccess) r = hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]);
+        if (r != hipSuccess) return hip_fail(r, "mfa_profile_read");
+        launches[p.kind[i]] += 1;
+        total_ms[p.kind[i]] += ms;
+        p.kind[i] = -1;
+    }
+    p.next = 0;
     return MFA_OK;
 }
 

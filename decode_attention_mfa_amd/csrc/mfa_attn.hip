@@ -25,6 +25,8 @@
 // Output of a chunk: if the sequence has one chunk, the final bf16 output and
 // lse; otherwise the chunk-normalised output (fp32) and its base-2 lse in the
 // workspace, merged by mfa_combine_kernel.
+#include <type_traits>
+
 #include "mfa_device.h"
 #include "mfa_internal.h"
 
@@ -37,13 +39,50 @@ __device__ __forceinline__ int vswz_bf16(int row) { return ((row >> 1) & 3) << 1
 // P rows in LDS: 64 heads x 64 tokens bf16 (128 B), chunk swizzle by head.
 __device__ __forceinline__ int pswz(int h) { return (h >> 1) & 7; }
 
-template <bool FP8>
-struct StepRegs {
-    static constexpr int NK = FP8 ? 4 : 8;   // 16-byte K pieces per lane
-    static constexpr int NV = FP8 ? 4 : 8;   // 16-byte V pieces per lane
-    u32x4 k[NK];
-    u32x4 v[NV];
-};
+// K rows of a wave's 16 tokens in LDS: 16-byte chunk c of row t is stored at
+// chunk position c ^ (t & 15), so the 16 lanes reading one chunk column of 16
+// rows hit 16 distinct bank groups.
+__device__ __forceinline__ int kswz(int row) { return row & 15; }
+
+// LDS stores issued as inline asm. The compiler treats any plain LDS store as
+// possibly overwriting bytes an LDS DMA is still filling and would wait for
+// every load in flight first; these stores go to buffers no DMA touches.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_store_b64(void* p, u32x2 v) {
+    asm volatile("ds_write_b64 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store_b32(void* p, uint32_t v) {
+    asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete,
+// then s_barrier. Unlike __syncthreads() it does not wait for the loads
+// still streaming into the LDS ring.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at lds_dst + 16*i (lds_dst is wave-uniform, passed in M0). Issued as inline
+// asm so that the compiler does not treat every later LDS access as possibly
+// overlapping the transfer (it would wait for all loads in flight before each
+// one); the ring's own waits (wait_vmem) order the reads instead. No register
+// is written, and the "memory" clobber keeps earlier reads of the slot ahead.
+__device__ __forceinline__ void dma_b128(const void* gsrc, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 ::"v"(gsrc), "s"(lds_dst) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+// The "memory" clobber keeps the compiler from moving LDS reads of the
+// DMA-filled ring above the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 
 template <bool FP8, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -51,18 +90,40 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     constexpr int ELEM = FP8 ? 1 : 2;
     constexpr int ROWB = kHeadDim * ELEM;          // bytes per cached row
     constexpr int VROWB = 64 * ELEM;               // bytes per row of a wave's V slice
-    constexpr int NK = StepRegs<FP8>::NK;
-    constexpr int NV = StepRegs<FP8>::NV;
+    constexpr int VSLOT = 64 * VROWB;              // one step of a wave's V slice
+    constexpr int KSLOT = 16 * ROWB;               // one step of a wave's K rows
+    constexpr int NK = KSLOT / 1024;               // 1 KB DMA instructions per step
+    constexpr int NV = VSLOT / 1024;
+    // vector-memory instructions a wave issues per step (all DMA into LDS)
+    constexpr int OPS_PER_STEP = NK + NV;
+    // steps in flight (current + prefetched): 3 x 32 KB for FP8, 2 x 64 KB for bf16
+    constexpr int RING = FP8 ? 3 : 2;
 
-    __shared__ __attribute__((aligned(16))) uint8_t vlds_all[4 * 64 * VROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t plds[kHeads * 64 * 2];
-    __shared__ float xchg[4][kHeads];
+    // One LDS object per ring slot: the compiler then sees that a read of one
+    // slot cannot alias the DMA still filling another, and waits only for the
+    // DMA of the slot it reads.
+    __shared__ __attribute__((aligned(1024))) uint8_t kr0[4][KSLOT], kr1[4][KSLOT], kr2[4][KSLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t vr0[4][VSLOT], vr1[4][VSLOT], vr2[4][VSLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t plds_all[2][kHeads * 64 * 2];
+    __shared__ __attribute__((aligned(16))) float xchg[4][kHeads];
+    __shared__ __attribute__((aligned(16))) float alpha_lds[kHeads];
+    __shared__ int flags_all[2][4];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63;
     const int lr = l & 15;
     const int g = l >> 4;
+    auto kring = [&](auto slot) -> uint8_t* {
+        if constexpr (decltype(slot)::value == 0) return kr0[w];
+        else if constexpr (decltype(slot)::value == 1) return kr1[w];
+        else return kr2[w];
+    };
+    auto vring = [&](auto slot) -> uint8_t* {
+        if constexpr (decltype(slot)::value == 0) return vr0[w];
+        else if constexpr (decltype(slot)::value == 1) return vr1[w];
+        else return vr2[w];
+    };
 
     const int b = blockIdx.x / p.n_chunk;
     const int c = blockIdx.x - b * p.n_chunk;
@@ -81,6 +142,7 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     }
     const int t_end = min(L, t_begin + p.chunk);
     const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
+    const int last_s = nsteps - 1;
     const bool single = (L + p.chunk - 1) / p.chunk == 1;
 
     // ---- Q as B operands: qop[ht][ks] holds Q[16ht + lr][d(ks, g, 0..7)] with
@@ -97,50 +159,33 @@ void mfa_attn_split_kernel(const AttnArgs p) {
                 qop[ht][ks] = *reinterpret_cast<const bf16x8*>(qb + (16 * ht + lr) * kHeadDim + d0);
             }
     }
+    // An empty asm that reads every Q register makes the compiler wait for the
+    // Q loads here, where nothing else is in flight; afterwards it has no load
+    // of its own outstanding and adds no waits of its own to the ring's.
+#pragma unroll
+    for (int ht = 0; ht < 4; ht++)
+        asm volatile("" ::"v"(qop[ht][0]), "v"(qop[ht][1]), "v"(qop[ht][2]), "v"(qop[ht][3]),
+                     "v"(qop[ht][4]), "v"(qop[ht][5]), "v"(qop[ht][6]), "v"(qop[ht][7]));
 
-    uint8_t* vlds = vlds_all + w * 64 * VROWB;
-
-    auto load_step = [&](int s, StepRegs<FP8>& r) {
-        const int t0 = t_begin + s * kStep;
+    // ---- issue the loads of step s (clamped to the last step, whose rows then
+    // hit in L2): this wave's 16 K rows and its V columns 64w..64w+63 of all 64
+    // tokens, both straight into its LDS ring slot. A DMA instruction writes
+    // lane i's 16 bytes at dst + 16*i, so each lane fetches the piece that
+    // belongs at that swizzled position.
+    auto issue_step = [&](int s, auto slot) {
+        const int t0 = t_begin + min(s, last_s) * kStep;
         const int last = t_end - 1 - t0;                 // last valid local token (>= 0)
         const int64_t base = kv_step_base<PAGED>(p.kv, b, t0);
-        {   // K rows of this wave's 16 tokens, MFMA A-operand layout
-            const int tl = min(16 * w + lr, last);
-            const uint8_t* row = p.kv.k + (base + tl) * ROWB;
+        uint8_t* ks = kring(slot);
 #pragma unroll
-            for (int i = 0; i < NK; i++) {
-                const int off = FP8 ? (64 * i + 16 * g) : (128 * (i >> 1) + 32 * g + 16 * (i & 1));
-                r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + off));
-            }
+        for (int i = 0; i < NK; i++) {
+            constexpr int RPI = 1024 / ROWB;             // rows per instruction
+            const int row = RPI * i + l / (ROWB / 16);
+            const int ch = (l % (ROWB / 16)) ^ kswz(row);
+            const uint8_t* src = p.kv.k + (base + min(16 * w + row, last)) * ROWB + 16 * ch;
+            dma_b128(src, lds_addr(ks + 1024 * i));
         }
-#pragma unroll
-        for (int i = 0; i < NV; i++) {  // V slice: columns 64w..64w+63 of all 64 tokens
-            const int tl = FP8 ? (16 * i + (l >> 2)) : (8 * i + (l >> 3));
-            const int ch = FP8 ? (l & 3) : (l & 7);
-            const uint8_t* row = p.kv.v + (base + min(tl, last)) * ROWB + 64 * w * ELEM;
-            r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 16 * ch));
-        }
-    };
-
-    // running state
-    float mq[4];        // running max (base 2) of heads 16ht + lr   (QK layout)
-    float lq[4];        // partial softmax denominators, same heads
-    float mp[4][4];     // running max of heads 16ht + 4g + i        (PV layout)
-    f32x4 o[4][4];      // O[16ht + 4g + i][64w + 16dt + lr]
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++) {
-        mq[ht] = -__builtin_inff();
-        lq[ht] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; i++) mp[ht][i] = -__builtin_inff();
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    auto compute_step = [&](int s, const StepRegs<FP8>& r) {
-        const int t0 = t_begin + s * kStep;
-        // (1) this wave's V slice -> LDS (its own region; program order keeps
-        // the previous step's reads ahead of these writes)
+        uint8_t* vs = vring(slot);
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             int row, ch;
@@ -151,17 +196,48 @@ void mfa_attn_split_kernel(const AttnArgs p) {
                 row = 8 * i + (l >> 3);
                 ch = (l & 7) ^ vswz_bf16(row);
             }
-            *reinterpret_cast<u32x4*>(vlds + row * VROWB + 16 * ch) = r.v[i];
+            const uint8_t* src = p.kv.v + (base + min(row, last)) * ROWB + 64 * w * ELEM + 16 * ch;
+            dma_b128(src, lds_addr(vs + 1024 * i));
         }
-        // (2) scores S^T[token 4g+i][head 16ht+lr] for this wave's 16 tokens
+    };
+
+    // running state (QK layout: heads 16ht + lr)
+    float mq[4];        // reference maxima (base 2)
+    float lq[4];        // partial softmax denominators
+    f32x4 o[4][4];      // O[16ht + 4g + i][64w + 16dt + lr]
+#pragma unroll
+    for (int ht = 0; ht < 4; ht++) {
+        mq[ht] = -__builtin_inff();
+        lq[ht] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    auto compute_step = [&](int s, auto slot) {
+        const int t0 = t_begin + s * kStep;
+        // K and V of step s have landed once at most the RING-1 younger steps'
+        // loads are in flight
+        wait_vmem<(RING - 1) * OPS_PER_STEP>();
+        // P and the vote flags alternate between two buffers by step parity:
+        // with one barrier per step a wave may write step s+1 while another
+        // still reads step s.
+        uint8_t* plds = plds_all[s & 1];
+        int* flags = flags_all[s & 1];
+        const uint8_t* vlds = vring(slot);
+        const uint8_t* klds = kring(slot) + lr * ROWB;   // this lane's K row
+        auto kpiece = [&](int c) {
+            return *reinterpret_cast<const u32x4*>(klds + 16 * (c ^ kswz(lr)));
+        };
+        // (1) scores S^T[token 4g+i][head 16ht+lr] for this wave's 16 tokens
         f32x4 sc[4];
 #pragma unroll
         for (int ht = 0; ht < 4; ht++) sc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (FP8) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const bf16x8 a0 = e4m3x8_to_bf16x8(r.k[i].x, r.k[i].y);
-                const bf16x8 a1 = e4m3x8_to_bf16x8(r.k[i].z, r.k[i].w);
+                const u32x4 kr = kpiece(4 * i + g);          // bytes 64i + 16g .. +16
+                const bf16x8 a0 = e4m3x8_to_bf16x8(kr.x, kr.y);
+                const bf16x8 a1 = e4m3x8_to_bf16x8(kr.z, kr.w);
 #pragma unroll
                 for (int ht = 0; ht < 4; ht++) {
                     sc[ht] = mfma16(a0, qop[ht][2 * i], sc[ht]);
@@ -171,80 +247,88 @@ void mfa_attn_split_kernel(const AttnArgs p) {
         } else {
 #pragma unroll
             for (int ks = 0; ks < 8; ks++) {
-                const bf16x8 a = bitcast<bf16x8>(r.k[ks]);
+                // bytes 128(ks/2) + 32g + 16(ks%2) .. +16
+                const bf16x8 a = bitcast<bf16x8>(kpiece(8 * (ks >> 1) + 2 * g + (ks & 1)));
 #pragma unroll
                 for (int ht = 0; ht < 4; ht++) sc[ht] = mfma16(a, qop[ht][ks], sc[ht]);
             }
         }
-        // (3) mask tokens past the chunk end, per-head max over the wave's tokens
-        const int valid = t_end - t0 - (16 * w + 4 * g);   // rows i < valid are real tokens
-        float mx[4];
+        // (2) mask tokens past the chunk end (last step of a chunk only)
+        if (t_end - t0 < kStep) {
+            const int valid = t_end - t0 - (16 * w + 4 * g);   // rows i < valid are real tokens
+#pragma unroll
+            for (int ht = 0; ht < 4; ht++)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    if (i >= valid) sc[ht][i] = -__builtin_inff();
+        }
+        // (3) optimistic P against the current reference maxima. A reference
+        // is kept until some score exceeds it by more than kTau (base 2), so
+        // P <= 2^kTau; the wave votes whether that happened.
+        bool over = false;
 #pragma unroll
         for (int ht = 0; ht < 4; ht++) {
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                if (i >= valid) sc[ht][i] = -__builtin_inff();
-            float m = fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3]));
-            m = fmaxf(m, __shfl_xor(m, 16));
-            m = fmaxf(m, __shfl_xor(m, 32));
-            mx[ht] = m * p.score_scale;
+            const float m = fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3]));
+            over |= m * p.score_scale > mq[ht] + kTau;
         }
-        if (g == 0) {
+        const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
+        float lstep[4];
+        auto write_p = [&]() {
 #pragma unroll
-            for (int ht = 0; ht < 4; ht++) xchg[w][16 * ht + lr] = mx[ht];
-        }
-        __syncthreads();
-        // (4) new running maxima, identical in every wave
-        float mq_new[4], alpha_q[4];
+            for (int ht = 0; ht < 4; ht++) {
+                float pr[4];
+                float sum = 0.f;
 #pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            const int h = 16 * ht + lr;
-            float m = fmaxf(fmaxf(xchg[0][h], xchg[1][h]), fmaxf(xchg[2][h], xchg[3][h]));
-            mq_new[ht] = fmaxf(mq[ht], m);
-            alpha_q[ht] = __builtin_amdgcn_exp2f(mq[ht] - mq_new[ht]);
-        }
-        float alpha_p[4][4];
+                for (int i = 0; i < 4; i++) {
+                    pr[i] = bf16_round(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[ht][i], p.score_scale, -mq[ht])));
+                    sum += pr[i];
+                }
+                lstep[ht] = sum;
+                const int h = 16 * ht + lr;
+                const int ch = (2 * w + (g >> 1)) ^ pswz(h);
+                lds_store_b64(plds + h * 128 + 16 * ch + 8 * (g & 1),
+                              u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
+            }
+        };
+        if (!wave_over) write_p();
+        if (l == 0) lds_store_b32(&flags[w], wave_over ? 1u : 0u);
+        lds_barrier();
+        const bool any_over = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+        if (!any_over) {
 #pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            const int h0 = 16 * ht + 4 * g;
-            const f32x4 x0 = *reinterpret_cast<const f32x4*>(&xchg[0][h0]);
-            const f32x4 x1 = *reinterpret_cast<const f32x4*>(&xchg[1][h0]);
-            const f32x4 x2 = *reinterpret_cast<const f32x4*>(&xchg[2][h0]);
-            const f32x4 x3 = *reinterpret_cast<const f32x4*>(&xchg[3][h0]);
+            for (int ht = 0; ht < 4; ht++) lq[ht] += lstep[ht];
+        } else {
+            // (4) rare: new references from every wave's maxima; rescale the
+            // denominators here and the outputs through alpha_lds; redo P
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float m = fmaxf(mp[ht][i], fmaxf(fmaxf(x0[i], x1[i]), fmaxf(x2[i], x3[i])));
-                alpha_p[ht][i] = __builtin_amdgcn_exp2f(mp[ht][i] - m);
-                mp[ht][i] = m;
+            for (int ht = 0; ht < 4; ht++) {
+                float m = fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3]));
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                if (g == 0) lds_store_b32(&xchg[w][16 * ht + lr], __builtin_bit_cast(uint32_t, m * p.score_scale));
+            }
+            lds_barrier();
+#pragma unroll
+            for (int ht = 0; ht < 4; ht++) {
+                const int h = 16 * ht + lr;
+                const float m = fmaxf(mq[ht], fmaxf(fmaxf(xchg[0][h], xchg[1][h]), fmaxf(xchg[2][h], xchg[3][h])));
+                const float a = __builtin_amdgcn_exp2f(mq[ht] - m);
+                lq[ht] *= a;
+                mq[ht] = m;
+                if (w == 0 && g == 0) lds_store_b32(&alpha_lds[h], __builtin_bit_cast(uint32_t, a));
+            }
+            write_p();
+#pragma unroll
+            for (int ht = 0; ht < 4; ht++) lq[ht] += lstep[ht];
+            lds_barrier();
+#pragma unroll
+            for (int ht = 0; ht < 4; ht++) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(&alpha_lds[16 * ht + 4 * g]);
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) o[ht][dt] *= a;
             }
         }
-        // (5) P = exp2(s2 - m), bf16; partial denominators from the rounded P
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            float pr[4];
-            float sum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ht][i], p.score_scale, -mq_new[ht]));
-                pr[i] = bf16_round(pr[i]);
-                sum += pr[i];
-            }
-            lq[ht] = lq[ht] * alpha_q[ht] + sum;
-            mq[ht] = mq_new[ht];
-            const int h = 16 * ht + lr;
-            const int ch = (2 * w + (g >> 1)) ^ pswz(h);
-            *reinterpret_cast<u32x2*>(plds + h * 128 + 16 * ch + 8 * (g & 1)) =
-                u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-        }
-        // (6) rescale the output accumulators to the new maxima
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++)
-#pragma unroll
-            for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) o[ht][dt][i] *= alpha_p[ht][i];
-        __syncthreads();
-        // (7) O[64 heads][64w..64w+63] += P[64 x 64 tok] . V[64 tok x 64]
+        // (5) O[64 heads][64w..64w+63] += P[64 x 64 tok] . V[64 tok x 64]
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {
             bf16x8 pa[4];
@@ -282,17 +366,39 @@ void mfa_attn_split_kernel(const AttnArgs p) {
         }
     };
 
-    // ---- main loop: two register sets, the next step loading during compute
-    StepRegs<FP8> ra, rb;
-    load_step(0, ra);
-    for (int s = 0; s < nsteps; s += 2) {
-        if (s + 1 < nsteps) load_step(s + 1, rb);
-        compute_step(s, ra);
-        if (s + 1 < nsteps) {
-            if (s + 2 < nsteps) load_step(s + 2, ra);
-            compute_step(s + 1, rb);
+    // ---- main loop: kRing steps in flight. Loads are issued unconditionally
+    // (past the last step they repeat its rows) so that every wait sees the
+    // same number of younger loads.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    if constexpr (RING == 3) {
+        issue_step(0, S0{});
+        issue_step(1, S1{});
+        for (int s = 0;; s += 3) {
+            issue_step(s + 2, S2{});
+            compute_step(s, S0{});
+            if (s + 1 >= nsteps) break;
+            issue_step(s + 3, S0{});
+            compute_step(s + 1, S1{});
+            if (s + 2 >= nsteps) break;
+            issue_step(s + 4, S1{});
+            compute_step(s + 2, S2{});
+            if (s + 3 >= nsteps) break;
+        }
+    } else {
+        issue_step(0, S0{});
+        for (int s = 0;; s += 2) {
+            issue_step(s + 1, S1{});
+            compute_step(s, S0{});
+            if (s + 1 >= nsteps) break;
+            issue_step(s + 2, S0{});
+            compute_step(s + 1, S1{});
+            if (s + 2 >= nsteps) break;
         }
     }
+    // drain the repeated loads before the workgroup exits
+    wait_vmem<0>();
 
     // ---- denominators: lanes -> wave (xor over g) -> workgroup (LDS)
 #pragma unroll
@@ -302,13 +408,27 @@ void mfa_attn_split_kernel(const AttnArgs p) {
         v += __shfl_xor(v, 32);
         lq[ht] = v;
     }
-    __syncthreads();   // all waves are done reading xchg
+    __syncthreads();   // all waves are done with xchg
     if (g == 0) {
 #pragma unroll
         for (int ht = 0; ht < 4; ht++) xchg[w][16 * ht + lr] = lq[ht];
     }
     __syncthreads();
 
+    // log-sum-exp (base 2) per head, from the QK layout of wave 0
+    if (w == 0 && g == 0) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ht++) {
+            const int h = 16 * ht + lr;
+            const float lsum = ((xchg[0][h] + xchg[1][h]) + xchg[2][h]) + xchg[3][h];
+            const float lse2 = mq[ht] + __builtin_amdgcn_logf(lsum);   // v_log_f32 is log2
+            if (single) {
+                if (p.lse_out) p.lse_out[b * kHeads + h] = lse2 * kLn2;
+            } else {
+                p.part_lse[((int64_t)b * p.n_chunk + c) * kHeads + h] = lse2;
+            }
+        }
+    }
     const int col = 64 * w + lr;
 #pragma unroll
     for (int ht = 0; ht < 4; ht++) {
@@ -320,21 +440,17 @@ void mfa_attn_split_kernel(const AttnArgs p) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int h = h0 + i;
-            const float lsum = ((l0[i] + l1[i]) + l2[i]) + l3[i];
-            const float inv = p.v_scale / lsum;
-            const float lse2 = mp[ht][i] + __builtin_amdgcn_logf(lsum);  // v_log_f32 is log2
+            const float inv = p.v_scale / (((l0[i] + l1[i]) + l2[i]) + l3[i]);
             if (single) {
                 uint16_t* orow = p.out + ((int64_t)b * kHeads + h) * kHeadDim + col;
 #pragma unroll
                 for (int dt = 0; dt < 4; dt++)
                     orow[16 * dt] = bitcast<uint16_t>((__bf16)(o[ht][dt][i] * inv));
-                if (p.lse_out && w == 0 && lr == 0) p.lse_out[b * kHeads + h] = lse2 * kLn2;
             } else {
                 const int64_t pidx = (int64_t)b * p.n_chunk + c;
                 float* prow = p.part_o + (pidx * kHeads + h) * kHeadDim + col;
 #pragma unroll
                 for (int dt = 0; dt < 4; dt++) prow[16 * dt] = o[ht][dt][i] * inv;
-                if (w == 0 && lr == 0) p.part_lse[pidx * kHeads + h] = lse2;
             }
         }
     }
@@ -390,7 +506,7 @@ __global__ __launch_bounds__(256) void mfa_gather_kernel(const KvView kv, int b,
     }
 }
 
-hipError_t launch_attention(const AttnArgs& a, bool fp8, bool paged, int batch, hipStream_t st) {
+hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch, hipStream_t st) {
     const dim3 grid(batch * a.n_chunk), block(256);
     if (fp8) {
         if (paged) hipLaunchKernelGGL((mfa_attn_split_kernel<true, true>), grid, block, 0, st, a);
@@ -399,8 +515,10 @@ hipError_t launch_attention(const AttnArgs& a, bool fp8, bool paged, int batch, 
         if (paged) hipLaunchKernelGGL((mfa_attn_split_kernel<false, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((mfa_attn_split_kernel<false, false>), grid, block, 0, st, a);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.n_chunk <= 1) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const AttnArgs& a, int batch, hipStream_t st) {
     hipLaunchKernelGGL(mfa_combine_kernel, dim3(batch * 16), dim3(256), 0, st, a);
     return hipGetLastError();
 }

@@ -24,6 +24,9 @@ constexpr int kHeadDim = 256;   // head dimension of Q, K and V
 constexpr int kPage = 64;       // tokens per cache page
 constexpr int kStep = 64;       // tokens per attention step (one page)
 constexpr float kLn2 = 0.69314718055994530942f;
+// Headroom (base-2 exponent) a score may exceed its head's reference maximum
+// before the reference is raised: unnormalised P stays <= 2^kTau.
+constexpr float kTau = 8.0f;
 
 template <typename T, typename S>
 __device__ __forceinline__ T bitcast(const S& s) {

@@ -22,7 +22,8 @@ struct AttnArgs {
     float v_scale;          // 1 for bf16
 };
 
-hipError_t launch_attention(const AttnArgs& a, bool fp8, bool paged, int batch, hipStream_t st);
+hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch, hipStream_t st);
+hipError_t launch_combine(const AttnArgs& a, int batch, hipStream_t st);
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
                          void* v_dst, hipStream_t st);
 
@@ -40,6 +41,8 @@ struct QprojArgs {
 
 constexpr int kQprojSplit = 8;   // K-splits of the down-projection
 
-hipError_t launch_qproj(const QprojArgs& a, hipStream_t st);
+hipError_t launch_qproj_down(const QprojArgs& a, hipStream_t st);
+hipError_t launch_rmsnorm(const QprojArgs& a, hipStream_t st);
+hipError_t launch_qproj_up(const QprojArgs& a, hipStream_t st);
 
 }  // namespace mfa

@@ -94,9 +94,10 @@ typedef struct {
 
 /* Create a handle for one layer shape. Validates `cfg` (host pointer) and
  * allocates the split-K workspace on the current device:
- *   max_batch * ceil(max_context / 64) * 64 * (256 + 1) * 4 bytes (partial
- *   outputs and log-sum-exps) plus the Q-projection scratch
- *   max_batch * q_rank * 4 bytes * 8.
+ *   max_batch * ceil(max_context / C) * 64 * (256 + 1) * 4 bytes of chunk
+ *   partials, C = split_tokens or, when that is 0, 256 (the smallest chunk
+ *   chosen per call), plus Q-projection scratch of max_batch * q_rank * 34
+ *   bytes.
  * On success stores the handle in *out (host pointer) and returns MFA_OK. */
 int mfa_create(const mfa_config* cfg, mfa_handle* out);
 
@@ -136,6 +137,28 @@ int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len);
  * cache type) with the same address generation mfa_decode uses. */
 int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, void* v_dst,
                         void* hip_stream);
+
+/* Kernel kinds reported by mfa_profile_read. */
+enum mfa_kernel_kind {
+    MFA_KERNEL_ATTENTION = 0,   /* chunked decode attention */
+    MFA_KERNEL_COMBINE = 1,     /* log-sum-exp merge of chunk partials */
+    MFA_KERNEL_QPROJ_DOWN = 2,  /* x . w_qa */
+    MFA_KERNEL_RMSNORM = 3,     /* bottleneck RMSNorm */
+    MFA_KERNEL_QPROJ_UP = 4,    /* chat . w_qb */
+    MFA_KERNEL_KINDS = 5
+};
+
+/* Per-kernel timing for benchmarks, off by default. While enabled, every
+ * kernel that mfa_decode or mfa_qproj launches is bracketed by a pair of
+ * hipEvents recorded on the call's stream (events are created here, on the
+ * current device). enable = 0 releases them. */
+int mfa_profile_enable(mfa_handle h, int enable);
+
+/* Wait for the launches recorded since the last read and return, per kernel
+ * kind (arrays of MFA_KERNEL_KINDS on the host), how many ran and their summed
+ * durations in milliseconds; then forget them. At most 4096 launches are kept
+ * between reads (older ones are overwritten). */
+int mfa_profile_read(mfa_handle h, int32_t* launches, double* total_ms);
 
 /* Release the handle and its workspace. NULL is accepted. The caller must
  * ensure no enqueued call that uses the handle is still running. */
