@@ -32,21 +32,22 @@
 
 namespace mfa {
 
-// V slice rows in LDS: 64 tokens x (64 columns * elem) bytes, 16-byte chunks
-// XOR-swizzled per row so that the transposed reads hit distinct banks.
-__device__ __forceinline__ int vswz_fp8(int row) { return (row >> 2) & 3; }
-__device__ __forceinline__ int vswz_bf16(int row) { return ((row >> 1) & 3) << 1; }
-// P rows in LDS: 64 heads x 64 tokens bf16 (128 B), chunk swizzle by head.
+// ---------------------------------------------------------------- LDS layout
+// Every 16-byte chunk c of a cached row r is stored at chunk position
+// c ^ swz(r) of that row, so that the reads of one chunk column across rows
+// spread over distinct bank groups:
+//   K (A-operand reads: 16 rows, one chunk each)      kswz(t) = t & 15
+//   V (transposed reads: 8 rows fp8 / 4 rows bf16)     vswz(r) = r & 7   (fp8)
+//                                                      vswz(r) = (r & 3) << 1 (bf16)
+//   P (64 heads x 64 tokens bf16, 128-byte rows)       pswz(h) = (h >> 1) & 7
+__device__ __forceinline__ int kswz(int t) { return t & 15; }
+template <bool FP8>
+__device__ __forceinline__ int vswz(int r) { return FP8 ? (r & 7) : ((r & 3) << 1); }
 __device__ __forceinline__ int pswz(int h) { return (h >> 1) & 7; }
 
-// K rows of a wave's 16 tokens in LDS: 16-byte chunk c of row t is stored at
-// chunk position c ^ (t & 15), so the 16 lanes reading one chunk column of 16
-// rows hit 16 distinct bank groups.
-__device__ __forceinline__ int kswz(int row) { return row & 15; }
-
-// LDS stores issued as inline asm. The compiler treats any plain LDS store as
-// possibly overwriting bytes an LDS DMA is still filling and would wait for
-// every load in flight first; these stores go to buffers no DMA touches.
+// LDS stores issued as inline asm. The compiler treats a plain LDS store as
+// possibly overwriting bytes an LDS DMA is still filling and would first wait
+// for every load in flight; these stores go to buffers no DMA touches.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -63,15 +64,23 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
-// at lds_dst + 16*i (lds_dst is wave-uniform, passed in M0). Issued as inline
-// asm so that the compiler does not treat every later LDS access as possibly
-// overlapping the transfer (it would wait for all loads in flight before each
-// one); the ring's own waits (wait_vmem) order the reads instead. No register
-// is written, and the "memory" clobber keeps earlier reads of the slot ahead.
-__device__ __forceinline__ void dma_b128(const void* gsrc, uint32_t lds_dst) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 ::"v"(gsrc), "s"(lds_dst) : "memory", "m0");
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes come
+// from sbase + voff and land at lds_dst + 16*i (lds_dst is wave-uniform and
+// goes through M0). Issued as inline asm so that the compiler does not treat
+// every later LDS access as possibly overlapping the transfer (it would wait
+// for all loads in flight before each one); the ring's own waits (wait_vmem)
+// order the reads instead. No register is written, and the "memory" clobber
+// keeps earlier reads of the slot ahead of it.
+__device__ __forceinline__ void dma_b128(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_dst) : "memory");
+}
+
+// A pointer every lane of the wave holds, moved to scalar registers.
+__device__ __forceinline__ const uint8_t* wave_uniform(const uint8_t* ptr) {
+    const uint64_t u = (uint64_t)(uintptr_t)ptr;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -83,30 +92,25 @@ __device__ __forceinline__ void wait_vmem() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-
 template <bool FP8, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mfa_attn_split_kernel(const AttnArgs p) {
     constexpr int ELEM = FP8 ? 1 : 2;
     constexpr int ROWB = kHeadDim * ELEM;          // bytes per cached row
-    constexpr int VROWB = 64 * ELEM;               // bytes per row of a wave's V slice
-    constexpr int VSLOT = 64 * VROWB;              // one step of a wave's V slice
-    constexpr int KSLOT = 16 * ROWB;               // one step of a wave's K rows
-    constexpr int NK = KSLOT / 1024;               // 1 KB DMA instructions per step
-    constexpr int NV = VSLOT / 1024;
-    // vector-memory instructions a wave issues per step (all DMA into LDS)
-    constexpr int OPS_PER_STEP = NK + NV;
-    // steps in flight (current + prefetched): 3 x 32 KB for FP8, 2 x 64 KB for bf16
-    constexpr int RING = FP8 ? 3 : 2;
+    constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
+    constexpr int RPI = 1024 / ROWB;               // rows per 1 KB DMA instruction
+    constexpr int KW = 16 * ROWB;                  // a wave's 16 rows of one step
+    constexpr int VT = kStep * ROWB;               // the V tile of one step
+    constexpr int NDMA = KW / 1024;                // DMA instructions per wave for K (same for V)
+    constexpr int OPS = 2 * NDMA;                  // vector-memory instructions per wave per step
+    // steps in flight: 4 x 32 KB (FP8) or 2 x 64 KB (bf16) of K + V
+    constexpr int RING = FP8 ? 4 : 2;
 
-    // One LDS object per ring slot: the compiler then sees that a read of one
-    // slot cannot alias the DMA still filling another, and waits only for the
-    // DMA of the slot it reads.
-    __shared__ __attribute__((aligned(1024))) uint8_t kr0[4][KSLOT], kr1[4][KSLOT], kr2[4][KSLOT];
-    __shared__ __attribute__((aligned(1024))) uint8_t vr0[4][VSLOT], vr1[4][VSLOT], vr2[4][VSLOT];
-    __shared__ __attribute__((aligned(16))) uint8_t plds_all[2][kHeads * 64 * 2];
+    __shared__ __attribute__((aligned(1024))) uint8_t kring[RING][4][KW];   // wave-private K rows
+    __shared__ __attribute__((aligned(1024))) uint8_t vring[RING][VT];      // shared V tile
+    __shared__ __attribute__((aligned(16))) uint8_t plds_all[2][kHeads * kStep * 2];
     __shared__ __attribute__((aligned(16))) float xchg[4][kHeads];
-    __shared__ __attribute__((aligned(16))) float alpha_lds[kHeads];
+    __shared__ __attribute__((aligned(16))) float xchg2[4][kHeads];
     __shared__ int flags_all[2][4];
 
     const int tid = threadIdx.x;
@@ -114,16 +118,6 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     const int l = tid & 63;
     const int lr = l & 15;
     const int g = l >> 4;
-    auto kring = [&](auto slot) -> uint8_t* {
-        if constexpr (decltype(slot)::value == 0) return kr0[w];
-        else if constexpr (decltype(slot)::value == 1) return kr1[w];
-        else return kr2[w];
-    };
-    auto vring = [&](auto slot) -> uint8_t* {
-        if constexpr (decltype(slot)::value == 0) return vr0[w];
-        else if constexpr (decltype(slot)::value == 1) return vr1[w];
-        else return vr2[w];
-    };
 
     const int b = blockIdx.x / p.n_chunk;
     const int c = blockIdx.x - b * p.n_chunk;
@@ -145,6 +139,52 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     const int last_s = nsteps - 1;
     const bool single = (L + p.chunk - 1) / p.chunk == 1;
 
+    // ---- DMA lane offsets (bytes from the step's first row; loop-invariant).
+    // Instruction i of wave w fills rows 16w + RPI*i + l/CPR; lane l lands at
+    // chunk position l % CPR of its row and so fetches the data chunk that the
+    // swizzle puts there.
+    uint32_t koff[NDMA], voff[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; i++) {
+        const int t = RPI * i + l / CPR;           // row within the wave's 16
+        const int r = 16 * w + t;                  // row within the step
+        koff[i] = r * ROWB + 16 * ((l % CPR) ^ kswz(t));
+        voff[i] = r * ROWB + 16 * ((l % CPR) ^ vswz<FP8>(r));
+    }
+
+    // ---- issue the loads of step s (clamped to the last step, whose rows then
+    // hit in L2) into ring slot s % RING: this wave's 16 K rows into its
+    // private region, and the same 16 rows of V into the shared V tile.
+    auto issue_step = [&](int s) {
+        const int t0 = t_begin + min(s, last_s) * kStep;
+        const int64_t base = kv_step_base<PAGED>(p.kv, b, t0);
+        const uint8_t* kb = wave_uniform(p.kv.k + base * ROWB);
+        const uint8_t* vb = wave_uniform(p.kv.v + base * ROWB);
+        const int slot = s % RING;
+        const uint32_t kd = __builtin_amdgcn_readfirstlane(lds_addr(kring[slot][w]));
+        const uint32_t vd = __builtin_amdgcn_readfirstlane(lds_addr(vring[slot]) + 16 * w * ROWB);
+        const int last = t_end - 1 - t0;           // last valid row of the step
+        if (last >= kStep - 1) {
+#pragma unroll
+            for (int i = 0; i < NDMA; i++) {
+                dma_b128(kb, koff[i], kd + 1024 * i);
+                dma_b128(vb, voff[i], vd + 1024 * i);
+            }
+        } else {   // partial last step: rows past the chunk end repeat the last row
+#pragma unroll
+            for (int i = 0; i < NDMA; i++) {
+                const int r = 16 * w + RPI * i + l / CPR;
+                const uint32_t shift = (uint32_t)((min(r, last) - r) * ROWB);
+                dma_b128(kb, koff[i] + shift, kd + 1024 * i);
+                dma_b128(vb, voff[i] + shift, vd + 1024 * i);
+            }
+        }
+    };
+
+    // The ring's first steps stream in while Q is fetched.
+#pragma unroll
+    for (int s = 0; s < RING - 1; s++) issue_step(s);
+
     // ---- Q as B operands: qop[ht][ks] holds Q[16ht + lr][d(ks, g, 0..7)] with
     // d(ks, g, j) = 64*(ks/2) + 16*g + 8*(ks%2) + j, the same d order the K
     // A operands use below.
@@ -160,84 +200,56 @@ void mfa_attn_split_kernel(const AttnArgs p) {
             }
     }
     // An empty asm that reads every Q register makes the compiler wait for the
-    // Q loads here, where nothing else is in flight; afterwards it has no load
-    // of its own outstanding and adds no waits of its own to the ring's.
+    // Q loads (and the DMAs issued before them) here; afterwards it has no
+    // load of its own outstanding and adds no waits of its own to the ring's.
 #pragma unroll
     for (int ht = 0; ht < 4; ht++)
         asm volatile("" ::"v"(qop[ht][0]), "v"(qop[ht][1]), "v"(qop[ht][2]), "v"(qop[ht][3]),
                      "v"(qop[ht][4]), "v"(qop[ht][5]), "v"(qop[ht][6]), "v"(qop[ht][7]));
 
-    // ---- issue the loads of step s (clamped to the last step, whose rows then
-    // hit in L2): this wave's 16 K rows and its V columns 64w..64w+63 of all 64
-    // tokens, both straight into its LDS ring slot. A DMA instruction writes
-    // lane i's 16 bytes at dst + 16*i, so each lane fetches the piece that
-    // belongs at that swizzled position.
-    auto issue_step = [&](int s, auto slot) {
-        const int t0 = t_begin + min(s, last_s) * kStep;
-        const int last = t_end - 1 - t0;                 // last valid local token (>= 0)
-        const int64_t base = kv_step_base<PAGED>(p.kv, b, t0);
-        uint8_t* ks = kring(slot);
+    // ---- per-pass state (QK layout: heads 16ht + lr). The reference maxima
+    // are fixed for a whole pass over the chunk: the exact maxima of the
+    // first step, raised to m_floor. A later score may exceed its reference
+    // by up to kTau (base 2), so unnormalised P <= 2^kTau and the output
+    // accumulators are never rescaled inside the loop. A larger excess, voted
+    // by any wave, restarts the chunk with the floor raised.
+    float mq[4];         // reference maxima (base 2)
+    float lq[4];         // partial softmax denominators of the rounded P
+    float le[4];         // partial softmax denominators of the unrounded P
+    float m_floor[4];    // lower bound for the references (from a restart)
+    f32x4 o[4][4];       // O[16ht + 4g + i][64w + 16dt + lr]
 #pragma unroll
-        for (int i = 0; i < NK; i++) {
-            constexpr int RPI = 1024 / ROWB;             // rows per instruction
-            const int row = RPI * i + l / (ROWB / 16);
-            const int ch = (l % (ROWB / 16)) ^ kswz(row);
-            const uint8_t* src = p.kv.k + (base + min(16 * w + row, last)) * ROWB + 16 * ch;
-            dma_b128(src, lds_addr(ks + 1024 * i));
-        }
-        uint8_t* vs = vring(slot);
+    for (int ht = 0; ht < 4; ht++) m_floor[ht] = -__builtin_inff();
+
+    auto clear_acc = [&]() {
 #pragma unroll
-        for (int i = 0; i < NV; i++) {
-            int row, ch;
-            if constexpr (FP8) {
-                row = 16 * i + (l >> 2);
-                ch = (l & 3) ^ vswz_fp8(row);
-            } else {
-                row = 8 * i + (l >> 3);
-                ch = (l & 7) ^ vswz_bf16(row);
-            }
-            const uint8_t* src = p.kv.v + (base + min(row, last)) * ROWB + 64 * w * ELEM + 16 * ch;
-            dma_b128(src, lds_addr(vs + 1024 * i));
+        for (int ht = 0; ht < 4; ht++) {
+            lq[ht] = 0.f;
+            le[ht] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
 
-    // running state (QK layout: heads 16ht + lr)
-    float mq[4];        // reference maxima (base 2)
-    float lq[4];        // partial softmax denominators
-    f32x4 o[4][4];      // O[16ht + 4g + i][64w + 16dt + lr]
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++) {
-        mq[ht] = -__builtin_inff();
-        lq[ht] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    auto compute_step = [&](int s, auto slot) {
+    // scores S^T[token 4g+i][head 16ht+lr] of this wave's 16 tokens of step s
+    // (its K rows have landed), tokens past the chunk end at -inf
+    auto qk = [&](int s, f32x4* sc) {
         const int t0 = t_begin + s * kStep;
-        // K and V of step s have landed once at most the RING-1 younger steps'
-        // loads are in flight
-        wait_vmem<(RING - 1) * OPS_PER_STEP>();
-        // P and the vote flags alternate between two buffers by step parity:
-        // with one barrier per step a wave may write step s+1 while another
-        // still reads step s.
-        uint8_t* plds = plds_all[s & 1];
-        int* flags = flags_all[s & 1];
-        const uint8_t* vlds = vring(slot);
-        const uint8_t* klds = kring(slot) + lr * ROWB;   // this lane's K row
-        auto kpiece = [&](int c) {
-            return *reinterpret_cast<const u32x4*>(klds + 16 * (c ^ kswz(lr)));
-        };
-        // (1) scores S^T[token 4g+i][head 16ht+lr] for this wave's 16 tokens
-        f32x4 sc[4];
+        const uint8_t* klds = kring[s % RING][w] + lr * ROWB;   // this lane's K row
+        u32x4 kp[FP8 ? 4 : 8];
+#pragma unroll
+        for (int i = 0; i < (FP8 ? 4 : 8); i++) {
+            // fp8: piece i = bytes 64i + 16g; bf16: bytes 128(i/2) + 32g + 16(i%2)
+            const int cidx = FP8 ? (4 * i + g) : (8 * (i >> 1) + 2 * g + (i & 1));
+            kp[i] = *reinterpret_cast<const u32x4*>(klds + 16 * (cidx ^ kswz(lr)));
+        }
 #pragma unroll
         for (int ht = 0; ht < 4; ht++) sc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (FP8) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const u32x4 kr = kpiece(4 * i + g);          // bytes 64i + 16g .. +16
-                const bf16x8 a0 = e4m3x8_to_bf16x8(kr.x, kr.y);
-                const bf16x8 a1 = e4m3x8_to_bf16x8(kr.z, kr.w);
+                const bf16x8 a0 = e4m3x8_to_bf16x8(kp[i].x, kp[i].y);
+                const bf16x8 a1 = e4m3x8_to_bf16x8(kp[i].z, kp[i].w);
 #pragma unroll
                 for (int ht = 0; ht < 4; ht++) {
                     sc[ht] = mfma16(a0, qop[ht][2 * i], sc[ht]);
@@ -247,14 +259,12 @@ void mfa_attn_split_kernel(const AttnArgs p) {
         } else {
 #pragma unroll
             for (int ks = 0; ks < 8; ks++) {
-                // bytes 128(ks/2) + 32g + 16(ks%2) .. +16
-                const bf16x8 a = bitcast<bf16x8>(kpiece(8 * (ks >> 1) + 2 * g + (ks & 1)));
+                const bf16x8 a = bitcast<bf16x8>(kp[ks]);
 #pragma unroll
                 for (int ht = 0; ht < 4; ht++) sc[ht] = mfma16(a, qop[ht][ks], sc[ht]);
             }
         }
-        // (2) mask tokens past the chunk end (last step of a chunk only)
-        if (t_end - t0 < kStep) {
+        if (t_end - t0 < kStep) {   // last step of the chunk only
             const int valid = t_end - t0 - (16 * w + 4 * g);   // rows i < valid are real tokens
 #pragma unroll
             for (int ht = 0; ht < 4; ht++)
@@ -262,9 +272,120 @@ void mfa_attn_split_kernel(const AttnArgs p) {
                 for (int i = 0; i < 4; i++)
                     if (i >= valid) sc[ht][i] = -__builtin_inff();
         }
-        // (3) optimistic P against the current reference maxima. A reference
-        // is kept until some score exceeds it by more than kTau (base 2), so
-        // P <= 2^kTau; the wave votes whether that happened.
+    };
+
+    // per-head maxima (base 2) of this step over all four waves, in QK layout
+    auto exchange_max = [&](const f32x4* sc, float* m_out) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ht++) {
+            float m = fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3]));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            if (g == 0) lds_store_b32(&xchg[w][16 * ht + lr], __builtin_bit_cast(uint32_t, m * p.score_scale));
+        }
+        lds_barrier();
+#pragma unroll
+        for (int ht = 0; ht < 4; ht++) {
+            const int h = 16 * ht + lr;
+            m_out[ht] = fmaxf(fmaxf(xchg[0][h], xchg[1][h]), fmaxf(xchg[2][h], xchg[3][h]));
+        }
+    };
+
+    // P = exp2(s2 - reference), rounded to bf16, into the step's P buffer.
+    // Two partial denominators: of the rounded P (normalises the output, so
+    // the weights applied to V sum to one) and of the unrounded P (gives the
+    // log-sum-exp to fp32 accuracy instead of bf16's 2^-8).
+    auto write_p = [&](int s, const f32x4* sc, float* lr_step, float* le_step) {
+        uint8_t* plds = plds_all[s & 1];
+#pragma unroll
+        for (int ht = 0; ht < 4; ht++) {
+            float e[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ht][i], p.score_scale, -mq[ht]));
+            const uint32_t p01 = pack_bf16x2(e[0], e[1]);
+            const uint32_t p23 = pack_bf16x2(e[2], e[3]);
+            lr_step[ht] = (__builtin_bit_cast(float, p01 << 16) + __builtin_bit_cast(float, p01 & 0xffff0000u)) +
+                          (__builtin_bit_cast(float, p23 << 16) + __builtin_bit_cast(float, p23 & 0xffff0000u));
+            le_step[ht] = (e[0] + e[1]) + (e[2] + e[3]);
+            const int h = 16 * ht + lr;
+            const int ch = (2 * w + (g >> 1)) ^ pswz(h);
+            lds_store_b64(plds + h * 128 + 16 * ch + 8 * (g & 1), u32x2{p01, p23});
+        }
+    };
+
+    // O[64 heads][64w..64w+63] += P[64 x 64 tok] . V[64 tok x 64w..64w+63];
+    // all LDS reads of the step are issued before the conversions and MFMAs
+    auto pv = [&](int s) {
+        const uint8_t* plds = plds_all[s & 1];
+        const uint8_t* vt = vring[s % RING];
+        bf16x8 pa[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+            for (int ht = 0; ht < 4; ht++) {
+                const int h = 16 * ht + lr;
+                pa[kk][ht] = *reinterpret_cast<const bf16x8*>(plds + h * 128 + 16 * ((4 * kk + g) ^ pswz(h)));
+            }
+        if constexpr (FP8) {
+            // lane j of a 16-lane group points at row r0 + j/2, bytes 8(j%2)..+7
+            // of chunk 4w + dt; it receives column 64w + 16dt + j of rows r0..r0+7
+            i32x2 vr[2][4];
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) {
+                    const int row = 32 * kk + 8 * g + (lr >> 1);
+                    const uint8_t* a = vt + row * ROWB + 16 * ((4 * w + dt) ^ vswz<FP8>(row)) + 8 * (lr & 1);
+                    vr[kk][dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i32x2*)(a));
+                }
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) {
+                    const bf16x8 vb = e4m3x8_to_bf16x8((uint32_t)vr[kk][dt].x, (uint32_t)vr[kk][dt].y);
+#pragma unroll
+                    for (int ht = 0; ht < 4; ht++) o[ht][dt] = mfma16(pa[kk][ht], vb, o[ht][dt]);
+                }
+        } else {
+            // two transposed reads of 4 rows each: lane j points at row
+            // r0 + j/4, elements 4(j%4)..+3 of the 16-column block
+            i16x4 vr[2][4][2];
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) {
+                        const int row = 32 * kk + 8 * g + 4 * hh + (lr >> 2);
+                        const int ch = 8 * w + 2 * dt + ((lr & 3) >> 1);
+                        const uint8_t* a = vt + row * ROWB + 16 * (ch ^ vswz<FP8>(row)) + 8 * (lr & 1);
+                        vr[kk][dt][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(a));
+                    }
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) {
+                    const u32x2 u0 = bitcast<u32x2>(vr[kk][dt][0]);
+                    const u32x2 u1 = bitcast<u32x2>(vr[kk][dt][1]);
+                    const bf16x8 vb = bitcast<bf16x8>(u32x4{u0.x, u0.y, u1.x, u1.y});
+#pragma unroll
+                    for (int ht = 0; ht < 4; ht++) o[ht][dt] = mfma16(pa[kk][ht], vb, o[ht][dt]);
+                }
+        }
+    };
+
+    // Step s > 0 against the fixed references. Returns true (in every wave)
+    // when some score exceeded its reference by more than kTau; m_floor then
+    // holds the raised bound and the step's P.V is skipped.
+    auto step = [&](int s) -> bool {
+        // this wave's K and V rows of step s have landed once at most the
+        // RING-2 younger steps' loads are in flight
+        wait_vmem<(RING - 2) * OPS>();
+        f32x4 sc[4];
+        qk(s, sc);
         bool over = false;
 #pragma unroll
         for (int ht = 0; ht < 4; ht++) {
@@ -272,146 +393,91 @@ void mfa_attn_split_kernel(const AttnArgs p) {
             over |= m * p.score_scale > mq[ht] + kTau;
         }
         const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
-        float lstep[4];
-        auto write_p = [&]() {
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) {
-                float pr[4];
-                float sum = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    pr[i] = bf16_round(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[ht][i], p.score_scale, -mq[ht])));
-                    sum += pr[i];
-                }
-                lstep[ht] = sum;
-                const int h = 16 * ht + lr;
-                const int ch = (2 * w + (g >> 1)) ^ pswz(h);
-                lds_store_b64(plds + h * 128 + 16 * ch + 8 * (g & 1),
-                              u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
-            }
-        };
-        if (!wave_over) write_p();
+        float lstep[4], estep[4];
+        write_p(s, sc, lstep, estep);
+        int* flags = flags_all[s & 1];
         if (l == 0) lds_store_b32(&flags[w], wave_over ? 1u : 0u);
+        // after this barrier: P of step s and every wave's V rows of step s
+        // are visible, and every wave is done with the P.V of step s-1
         lds_barrier();
-        const bool any_over = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
-        if (!any_over) {
+        if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
+            float m[4];
+            exchange_max(sc, m);
 #pragma unroll
-            for (int ht = 0; ht < 4; ht++) lq[ht] += lstep[ht];
-        } else {
-            // (4) rare: new references from every wave's maxima; rescale the
-            // denominators here and the outputs through alpha_lds; redo P
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) {
-                float m = fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3]));
-                m = fmaxf(m, __shfl_xor(m, 16));
-                m = fmaxf(m, __shfl_xor(m, 32));
-                if (g == 0) lds_store_b32(&xchg[w][16 * ht + lr], __builtin_bit_cast(uint32_t, m * p.score_scale));
-            }
-            lds_barrier();
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) {
-                const int h = 16 * ht + lr;
-                const float m = fmaxf(mq[ht], fmaxf(fmaxf(xchg[0][h], xchg[1][h]), fmaxf(xchg[2][h], xchg[3][h])));
-                const float a = __builtin_amdgcn_exp2f(mq[ht] - m);
-                lq[ht] *= a;
-                mq[ht] = m;
-                if (w == 0 && g == 0) lds_store_b32(&alpha_lds[h], __builtin_bit_cast(uint32_t, a));
-            }
-            write_p();
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) lq[ht] += lstep[ht];
-            lds_barrier();
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(&alpha_lds[16 * ht + 4 * g]);
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++) o[ht][dt] *= a;
-            }
+            for (int ht = 0; ht < 4; ht++) m_floor[ht] = fmaxf(mq[ht], m[ht]);
+            lds_barrier();   // everyone has read xchg before it is reused
+            // The next pass starts from zero. Clearing here (not at the top
+            // of the pass) leaves the accumulators entering this step with a
+            // single use, the P.V MFMA, so it can accumulate in place.
+            clear_acc();
+            return true;
         }
-        // (5) O[64 heads][64w..64w+63] += P[64 x 64 tok] . V[64 tok x 64]
+        // ring slot (s-1) % RING is free now: refill it
+        issue_step(s + RING - 1);
 #pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-            bf16x8 pa[4];
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) {
-                const int h = 16 * ht + lr;
-                pa[ht] = *reinterpret_cast<const bf16x8*>(plds + h * 128 + 16 * ((4 * kk + g) ^ pswz(h)));
-            }
-#pragma unroll
-            for (int dt = 0; dt < 4; dt++) {
-                bf16x8 vb;
-                if constexpr (FP8) {
-                    const int row = 32 * kk + 8 * g + (lr >> 1);
-                    const uint8_t* a = vlds + row * VROWB + 16 * (dt ^ vswz_fp8(row)) + 8 * (lr & 1);
-                    const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (__attribute__((address_space(3))) i32x2*)(a));
-                    vb = e4m3x8_to_bf16x8((uint32_t)raw.x, (uint32_t)raw.y);
-                } else {
-                    const int ch = 2 * dt + ((lr & 3) >> 1);
-                    const int row0 = 32 * kk + 8 * g + (lr >> 2);
-                    const int row1 = row0 + 4;
-                    const uint8_t* a0 = vlds + row0 * VROWB + 16 * (ch ^ vswz_bf16(row0)) + 8 * (lr & 1);
-                    const uint8_t* a1 = vlds + row1 * VROWB + 16 * (ch ^ vswz_bf16(row1)) + 8 * (lr & 1);
-                    const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(a0));
-                    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(a1));
-                    const u32x2 u0 = bitcast<u32x2>(r0);
-                    const u32x2 u1 = bitcast<u32x2>(r1);
-                    vb = bitcast<bf16x8>(u32x4{u0.x, u0.y, u1.x, u1.y});
-                }
-#pragma unroll
-                for (int ht = 0; ht < 4; ht++) o[ht][dt] = mfma16(pa[ht], vb, o[ht][dt]);
-            }
+        for (int ht = 0; ht < 4; ht++) {
+            lq[ht] += lstep[ht];
+            le[ht] += estep[ht];
         }
+        pv(s);
+        return false;
     };
 
-    // ---- main loop: kRing steps in flight. Loads are issued unconditionally
-    // (past the last step they repeat its rows) so that every wait sees the
-    // same number of younger loads.
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    if constexpr (RING == 3) {
-        issue_step(0, S0{});
-        issue_step(1, S1{});
-        for (int s = 0;; s += 3) {
-            issue_step(s + 2, S2{});
-            compute_step(s, S0{});
-            if (s + 1 >= nsteps) break;
-            issue_step(s + 3, S0{});
-            compute_step(s + 1, S1{});
-            if (s + 2 >= nsteps) break;
-            issue_step(s + 4, S1{});
-            compute_step(s + 2, S2{});
-            if (s + 3 >= nsteps) break;
+    clear_acc();
+    for (int pass = 0;; pass++) {   // one pass over the chunk; repeated only after a vote
+        // Loads are issued unconditionally (past the last step they repeat
+        // its rows) so that every wait sees the same number of younger loads.
+        if (pass > 0) {
+#pragma unroll
+            for (int s = 0; s < RING - 1; s++) issue_step(s);
         }
-    } else {
-        issue_step(0, S0{});
-        for (int s = 0;; s += 2) {
-            issue_step(s + 1, S1{});
-            compute_step(s, S0{});
-            if (s + 1 >= nsteps) break;
-            issue_step(s + 2, S0{});
-            compute_step(s + 1, S1{});
-            if (s + 2 >= nsteps) break;
+        {   // step 0 sets the references from its exact maxima
+            wait_vmem<(RING - 2) * OPS>();
+            f32x4 sc[4];
+            qk(0, sc);
+            float m[4];
+            exchange_max(sc, m);
+#pragma unroll
+            for (int ht = 0; ht < 4; ht++) mq[ht] = fmaxf(m_floor[ht], m[ht]);
+            float lstep[4], estep[4];
+            write_p(0, sc, lstep, estep);
+            lds_barrier();
+            issue_step(RING - 1);
+#pragma unroll
+            for (int ht = 0; ht < 4; ht++) {
+                lq[ht] += lstep[ht];
+                le[ht] += estep[ht];
+            }
+            pv(0);
         }
+        bool restart = false;
+        for (int s = 1; s < nsteps; s++)
+            if ((restart = step(s))) break;
+        // drain the ring's loads (the repeated ones too) before the next pass
+        // or the exit
+        wait_vmem<0>();
+        if (!restart) break;
+        lds_barrier();   // no wave still reads the ring or P of the pass
     }
-    // drain the repeated loads before the workgroup exits
-    wait_vmem<0>();
 
     // ---- denominators: lanes -> wave (xor over g) -> workgroup (LDS)
 #pragma unroll
     for (int ht = 0; ht < 4; ht++) {
-        float v = lq[ht];
+        float v = lq[ht], u = le[ht];
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
+        u += __shfl_xor(u, 16);
+        u += __shfl_xor(u, 32);
         lq[ht] = v;
+        le[ht] = u;
     }
     __syncthreads();   // all waves are done with xchg
     if (g == 0) {
 #pragma unroll
-        for (int ht = 0; ht < 4; ht++) xchg[w][16 * ht + lr] = lq[ht];
+        for (int ht = 0; ht < 4; ht++) {
+            xchg[w][16 * ht + lr] = lq[ht];
+            xchg2[w][16 * ht + lr] = le[ht];
+        }
     }
     __syncthreads();
 
@@ -420,7 +486,7 @@ void mfa_attn_split_kernel(const AttnArgs p) {
 #pragma unroll
         for (int ht = 0; ht < 4; ht++) {
             const int h = 16 * ht + lr;
-            const float lsum = ((xchg[0][h] + xchg[1][h]) + xchg[2][h]) + xchg[3][h];
+            const float lsum = ((xchg2[0][h] + xchg2[1][h]) + xchg2[2][h]) + xchg2[3][h];
             const float lse2 = mq[ht] + __builtin_amdgcn_logf(lsum);   // v_log_f32 is log2
             if (single) {
                 if (p.lse_out) p.lse_out[b * kHeads + h] = lse2 * kLn2;

@@ -25,8 +25,9 @@ constexpr int kPage = 64;       // tokens per cache page
 constexpr int kStep = 64;       // tokens per attention step (one page)
 constexpr float kLn2 = 0.69314718055994530942f;
 // Headroom (base-2 exponent) a score may exceed its head's reference maximum
-// before the reference is raised: unnormalised P stays <= 2^kTau.
-constexpr float kTau = 8.0f;
+// before the chunk is redone with a higher reference: unnormalised P stays
+// <= 2^kTau, so with |V| < 2^64 the fp32 accumulators cannot overflow.
+constexpr float kTau = 48.0f;
 
 template <typename T, typename S>
 __device__ __forceinline__ T bitcast(const S& s) {

@@ -17,7 +17,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-2        # row-wise normwise relative error of the bf16 output
-LSE_TOL = 2e-3    # absolute, natural log
+LSE_TOL = 1e-3    # absolute, natural log
 
 
 def _say(*a):
@@ -199,3 +199,27 @@ def test_host_errors_enqueue_nothing():
         assert "scale" in str(ei.value)
     finally:
         m.mfa_destroy(h)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_dominant_late_keys_restart(kv):
+    """Keys planted late in a sequence whose scores exceed everything before
+    them by far more than the kernel's headroom: the chunk must be redone with
+    a higher reference (twice here) and still match the oracle."""
+    B, L = 2, 1500
+    case = synth.make_case("dominant", B, [L, 900], "bf16", seed=82)
+    q = oracle.case_q(case)
+    K = oracle.decode_bf16(case.k).astype(np.float32)
+    for b, t, c in ((0, 700, 3.0), (0, 1300, 6.0), (1, 400, 5.0)):
+        K[b, t] = (c * q[b, 5]).astype(np.float32)        # head 5: score ~ c*|q|^2/16
+    if kv == "bf16":
+        case.k = synth.bf16_bits(K)
+    else:
+        V = oracle.decode_bf16(case.v).astype(np.float32)
+        ks = float(np.float32(np.abs(K).max() / 448.0))
+        vs = float(np.float32(np.abs(V).max() / 448.0))
+        case = synth.Case(name="dominant-fp8", batch=B, kv_dtype="fp8", seq_lens=case.seq_lens,
+                          k=synth.e4m3_codes(K / np.float32(ks)), v=synth.e4m3_codes(V / np.float32(vs)),
+                          q=case.q, k_scale=ks, v_scale=vs)
+    for split in (0, 512):
+        check_parity(case, split_tokens=split, label=f"dominant late keys {kv} split={split}")
