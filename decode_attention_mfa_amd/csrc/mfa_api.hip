@@ -35,8 +35,8 @@ constexpr int kMaxAutoSplit = 2048;
 
 }  // namespace
 
-// Optional per-kernel timing: a ring of hipEvent pairs recorded around each
-// launch on the call's stream.
+// Optional per-kernel timing: a ring of hipEvent pairs, each pair stamped
+// with one kernel's start and end by the launch itself.
 struct Profiler {
     static constexpr int kCap = 4096;
     bool on = false;
@@ -54,24 +54,25 @@ struct mfa_ctx {
     int max_chunks;        // per sequence, at the smallest chunk this handle may use
     float* part_o;         // [max_batch * max_chunks][64][256]
     float* part_lse;       // [max_batch * max_chunks][64]
+    int32_t* counters;     // [max_batch], zero between calls
     float* c_part;         // [kQprojSplit][max_batch][q_rank]
     uint16_t* chat;        // [max_batch][q_rank]
 };
 
 static bool valid_handle(mfa_handle h) { return h != nullptr && h->magic == kMagic; }
 
-// Launch `fn` on `st`, bracketed by a profiling event pair when enabled.
+// Launch `fn(launch)` on `st`; when profiling is on, with the next event pair
+// of the ring attached to the kernel's own start and end.
 template <typename F>
 static hipError_t timed_launch(mfa_ctx* h, int kind, hipStream_t st, F&& fn) {
     Profiler& p = h->prof;
-    if (!p.on) return fn();
+    mfa::Launch l{st};
+    if (!p.on) return fn(l);
     const int i = p.next;
     p.next = (p.next + 1) % Profiler::kCap;
-    hipError_t e = hipEventRecord(p.ev[2 * i], st);
-    if (e != hipSuccess) return e;
-    e = fn();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(p.ev[2 * i + 1], st);
+    l.start = p.ev[2 * i];
+    l.stop = p.ev[2 * i + 1];
+    const hipError_t e = fn(l);
     if (e == hipSuccess) p.kind[i] = kind;
     return e;
 }
@@ -161,9 +162,9 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
         delete h;
         return hip_fail(e, "mfa_create: device query");
     }
-    void* p[4] = {nullptr, nullptr, nullptr, nullptr};
-    const int64_t sizes[4] = {bytes_o, bytes_lse, bytes_c, bytes_chat};
-    for (int i = 0; i < 4; i++) {
+    void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    const int64_t sizes[5] = {bytes_o, bytes_lse, bytes_c, bytes_chat, (int64_t)c.max_batch * 4};
+    for (int i = 0; i < 5; i++) {
         e = hipMalloc(&p[i], (size_t)sizes[i]);
         if (e != hipSuccess) {
             for (int j = 0; j < i; j++) (void)hipFree(p[j]);
@@ -177,6 +178,14 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     h->part_lse = (float*)p[1];
     h->c_part = (float*)p[2];
     h->chat = (uint16_t*)p[3];
+    h->counters = (int32_t*)p[4];
+    e = hipMemset(h->counters, 0, (size_t)c.max_batch * 4);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        for (int j = 0; j < 5; j++) (void)hipFree(p[j]);
+        delete h;
+        return hip_fail(e, "mfa_create: clearing the workspace");
+    }
     h->magic = kMagic;
     *out = h;
     return MFA_OK;
@@ -192,6 +201,7 @@ int mfa_destroy(mfa_handle h) {
     (void)hipFree(h->part_lse);
     (void)hipFree(h->c_part);
     (void)hipFree(h->chat);
+    (void)hipFree(h->counters);
     delete h;
     return MFA_OK;
 }
@@ -225,9 +235,9 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w, 
     a.ksplit = mfa::kQprojSplit;
     a.eps = h->cfg.rms_eps;
     hipStream_t st = (hipStream_t)hip_stream;
-    hipError_t e = timed_launch(h, MFA_KERNEL_QPROJ_DOWN, st, [&] { return mfa::launch_qproj_down(a, st); });
-    if (e == hipSuccess) e = timed_launch(h, MFA_KERNEL_RMSNORM, st, [&] { return mfa::launch_rmsnorm(a, st); });
-    if (e == hipSuccess) e = timed_launch(h, MFA_KERNEL_QPROJ_UP, st, [&] { return mfa::launch_qproj_up(a, st); });
+    hipError_t e = timed_launch(h, MFA_KERNEL_QPROJ_DOWN, st, [&](const mfa::Launch& l) { return mfa::launch_qproj_down(a, l); });
+    if (e == hipSuccess) e = timed_launch(h, MFA_KERNEL_RMSNORM, st, [&](const mfa::Launch& l) { return mfa::launch_rmsnorm(a, l); });
+    if (e == hipSuccess) e = timed_launch(h, MFA_KERNEL_QPROJ_UP, st, [&](const mfa::Launch& l) { return mfa::launch_qproj_up(a, l); });
     if (e != hipSuccess) return hip_fail(e, "mfa_qproj: launch");
     return MFA_OK;
 }
@@ -290,20 +300,22 @@ int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* 
     a.lse_out = lse_out;
     a.part_o = h->part_o;
     a.part_lse = h->part_lse;
+    a.counters = h->counters;
     a.chunk = choose_split(h, batch, max_len);
     a.n_chunk = (max_len + a.chunk - 1) / a.chunk;
     if (a.n_chunk < 1) a.n_chunk = 1;
     if (a.n_chunk > h->max_chunks)
         return fail(MFA_ERR_INVALID, "mfa_decode: %d chunks exceed the workspace (%d)", a.n_chunk, h->max_chunks);
+    a.fuse_max = a.n_chunk <= mfa::kFusedMaxChunks ? mfa::kFusedMaxChunks : 1;
     const float log2e = 1.4426950408889634f;
     a.score_scale = h->cfg.softmax_scale * (fp8 ? kv->k_scale : 1.0f) * log2e;
     a.v_scale = fp8 ? kv->v_scale : 1.0f;
     hipStream_t st = (hipStream_t)hip_stream;
     const bool paged = h->cfg.page_size != 0;
     hipError_t e = timed_launch(h, MFA_KERNEL_ATTENTION, st,
-                                [&] { return mfa::launch_attn_split(a, fp8, paged, batch, st); });
-    if (e == hipSuccess && a.n_chunk > 1)
-        e = timed_launch(h, MFA_KERNEL_COMBINE, st, [&] { return mfa::launch_combine(a, batch, st); });
+                                [&](const mfa::Launch& l) { return mfa::launch_attn_split(a, fp8, paged, batch, l); });
+    if (e == hipSuccess && a.n_chunk > a.fuse_max)
+        e = timed_launch(h, MFA_KERNEL_COMBINE, st, [&](const mfa::Launch& l) { return mfa::launch_combine(a, batch, l); });
     if (e != hipSuccess) return hip_fail(e, "mfa_decode: launch");
     return MFA_OK;
 }
@@ -319,7 +331,7 @@ int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, 
     if (b < 0 || b >= h->cfg.max_batch)
         return fail(MFA_ERR_INVALID, "mfa_debug_gather_kv: sequence %d outside [0, %d)", b, h->cfg.max_batch);
     hipError_t e = mfa::launch_gather(make_view(h, kv, max_len), h->cfg.page_size != 0, b, max_len, k_dst, v_dst,
-                                      (hipStream_t)hip_stream);
+                                      mfa::Launch{(hipStream_t)hip_stream});
     if (e != hipSuccess) return hip_fail(e, "mfa_debug_gather_kv: launch");
     return MFA_OK;
 }
@@ -336,7 +348,7 @@ int mfa_profile_enable(mfa_handle h, int enable) {
     p.ev.assign(2 * Profiler::kCap, nullptr);
     p.kind.assign(Profiler::kCap, -1);
     for (auto& e : p.ev) {
-        hipError_t r = hipEventCreate(&e);
+        hipError_t r = hipEventCreateWithFlags(&e, hipEventReleaseToDevice);
         if (r != hipSuccess) {
             profiler_release(p);
             return hip_fail(r, "mfa_profile_enable: hipEventCreate");

@@ -54,6 +54,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void lds_store_b64(void* p, u32x2 v) {
     asm volatile("ds_write_b64 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
 }
+__device__ __forceinline__ void lds_store_b128(void* p, u32x4 v) {
+    asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
 __device__ __forceinline__ void lds_store_b32(void* p, uint32_t v) {
     asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
 }
@@ -83,6 +86,30 @@ __device__ __forceinline__ const uint8_t* wave_uniform(const uint8_t* ptr) {
     return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Device-coherent (agent scope, sc1) 16-byte store and loads: they bypass the
+// per-XCD L2, so a workgroup on another XCD sees the data once the store is
+// acknowledged. The loads are issued as one asm block that also waits for
+// them, so no output register is left pending when the block ends.
+__device__ __forceinline__ void coherent_store_b128(f32x4* ptr, f32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(ptr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void coherent_load_b128x8(f32x4* v, const f32x4* src, int stride) {
+    asm volatile(
+        "global_load_dwordx4 %0, %8, off sc1\n\t"
+        "global_load_dwordx4 %1, %9, off sc1\n\t"
+        "global_load_dwordx4 %2, %10, off sc1\n\t"
+        "global_load_dwordx4 %3, %11, off sc1\n\t"
+        "global_load_dwordx4 %4, %12, off sc1\n\t"
+        "global_load_dwordx4 %5, %13, off sc1\n\t"
+        "global_load_dwordx4 %6, %14, off sc1\n\t"
+        "global_load_dwordx4 %7, %15, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(src), "v"(src + stride), "v"(src + 2 * stride), "v"(src + 3 * stride), "v"(src + 4 * stride),
+          "v"(src + 5 * stride), "v"(src + 6 * stride), "v"(src + 7 * stride)
+        : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 // The "memory" clobber keeps the compiler from moving LDS reads of the
 // DMA-filled ring above the wait.
@@ -106,12 +133,18 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     // steps in flight: 4 x 32 KB (FP8) or 2 x 64 KB (bf16) of K + V
     constexpr int RING = FP8 ? 4 : 2;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t kring[RING][4][KW];   // wave-private K rows
-    __shared__ __attribute__((aligned(1024))) uint8_t vring[RING][VT];      // shared V tile
-    __shared__ __attribute__((aligned(16))) uint8_t plds_all[2][kHeads * kStep * 2];
+    // LDS: the ring (slot-major: four waves' K rows, then the V tile), then
+    // the two P buffers. Slot RING-1 doubles as the staging area for Q.
+    constexpr int SLOT = 4 * KW + VT;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[RING * SLOT + 2 * kHeads * kStep * 2];
     __shared__ __attribute__((aligned(16))) float xchg[4][kHeads];
     __shared__ __attribute__((aligned(16))) float xchg2[4][kHeads];
     __shared__ int flags_all[2][4];
+    __shared__ int arrival;
+    __shared__ float lse_lds[kHeads];
+    auto kring = [&](int slot, int wave) -> uint8_t* { return smem + slot * SLOT + wave * KW; };
+    auto vring = [&](int slot) -> uint8_t* { return smem + slot * SLOT + 4 * KW; };
+    auto plds_of = [&](int parity) -> uint8_t* { return smem + RING * SLOT + parity * (kHeads * kStep * 2); };
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -161,8 +194,8 @@ void mfa_attn_split_kernel(const AttnArgs p) {
         const uint8_t* kb = wave_uniform(p.kv.k + base * ROWB);
         const uint8_t* vb = wave_uniform(p.kv.v + base * ROWB);
         const int slot = s % RING;
-        const uint32_t kd = __builtin_amdgcn_readfirstlane(lds_addr(kring[slot][w]));
-        const uint32_t vd = __builtin_amdgcn_readfirstlane(lds_addr(vring[slot]) + 16 * w * ROWB);
+        const uint32_t kd = __builtin_amdgcn_readfirstlane(lds_addr(kring(slot, w)));
+        const uint32_t vd = __builtin_amdgcn_readfirstlane(lds_addr(vring(slot)) + 16 * w * ROWB);
         const int last = t_end - 1 - t0;           // last valid row of the step
         if (last >= kStep - 1) {
 #pragma unroll
@@ -185,27 +218,36 @@ void mfa_attn_split_kernel(const AttnArgs p) {
 #pragma unroll
     for (int s = 0; s < RING - 1; s++) issue_step(s);
 
-    // ---- Q as B operands: qop[ht][ks] holds Q[16ht + lr][d(ks, g, 0..7)] with
-    // d(ks, g, j) = 64*(ks/2) + 16*g + 8*(ks%2) + j, the same d order the K
-    // A operands use below.
+    // ---- Q, fetched once per workgroup: wave w copies heads 16w..16w+15 into
+    // the staging area (16-byte chunk c of head h at position c ^ (h & 15)),
+    // then every wave reads its B operands: qop[ht][ks] holds
+    // Q[16ht + lr][d(ks, g, 0..7)] with d(ks, g, j) = 64*(ks/2) + 16*g +
+    // 8*(ks%2) + j, the same d order the K A operands use below.
     bf16x8 qop[4][8];
     {
+        uint8_t* qs = smem + (RING - 1) * SLOT;
         const uint16_t* qb = p.q + (int64_t)b * kHeads * kHeadDim;
+        u32x4 qv[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int h = 16 * w + 2 * i + (l >> 5);
+            qv[i] = *reinterpret_cast<const u32x4*>(qb + h * kHeadDim + 8 * (l & 31));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int h = 16 * w + 2 * i + (l >> 5);
+            lds_store_b128(qs + h * 512 + 16 * ((l & 31) ^ (h & 15)), qv[i]);
+        }
+        lds_barrier();
 #pragma unroll
         for (int ht = 0; ht < 4; ht++)
 #pragma unroll
             for (int ks = 0; ks < 8; ks++) {
-                const int d0 = 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
-                qop[ht][ks] = *reinterpret_cast<const bf16x8*>(qb + (16 * ht + lr) * kHeadDim + d0);
+                const int h = 16 * ht + lr;
+                const int cq = 8 * (ks >> 1) + 2 * g + (ks & 1);
+                qop[ht][ks] = *reinterpret_cast<const bf16x8*>(qs + h * 512 + 16 * (cq ^ (h & 15)));
             }
     }
-    // An empty asm that reads every Q register makes the compiler wait for the
-    // Q loads (and the DMAs issued before them) here; afterwards it has no
-    // load of its own outstanding and adds no waits of its own to the ring's.
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++)
-        asm volatile("" ::"v"(qop[ht][0]), "v"(qop[ht][1]), "v"(qop[ht][2]), "v"(qop[ht][3]),
-                     "v"(qop[ht][4]), "v"(qop[ht][5]), "v"(qop[ht][6]), "v"(qop[ht][7]));
 
     // ---- per-pass state (QK layout: heads 16ht + lr). The reference maxima
     // are fixed for a whole pass over the chunk: the exact maxima of the
@@ -235,7 +277,7 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     // (its K rows have landed), tokens past the chunk end at -inf
     auto qk = [&](int s, f32x4* sc) {
         const int t0 = t_begin + s * kStep;
-        const uint8_t* klds = kring[s % RING][w] + lr * ROWB;   // this lane's K row
+        const uint8_t* klds = kring(s % RING, w) + lr * ROWB;   // this lane's K row
         u32x4 kp[FP8 ? 4 : 8];
 #pragma unroll
         for (int i = 0; i < (FP8 ? 4 : 8); i++) {
@@ -296,7 +338,7 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     // the weights applied to V sum to one) and of the unrounded P (gives the
     // log-sum-exp to fp32 accuracy instead of bf16's 2^-8).
     auto write_p = [&](int s, const f32x4* sc, float* lr_step, float* le_step) {
-        uint8_t* plds = plds_all[s & 1];
+        uint8_t* plds = plds_of(s & 1);
 #pragma unroll
         for (int ht = 0; ht < 4; ht++) {
             float e[4];
@@ -317,8 +359,8 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     // O[64 heads][64w..64w+63] += P[64 x 64 tok] . V[64 tok x 64w..64w+63];
     // all LDS reads of the step are issued before the conversions and MFMAs
     auto pv = [&](int s) {
-        const uint8_t* plds = plds_all[s & 1];
-        const uint8_t* vt = vring[s % RING];
+        const uint8_t* plds = plds_of(s & 1);
+        const uint8_t* vt = vring(s % RING);
         bf16x8 pa[2][4];
 #pragma unroll
         for (int kk = 0; kk < 2; kk++)
@@ -481,21 +523,20 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     }
     __syncthreads();
 
-    // log-sum-exp (base 2) per head, from the QK layout of wave 0
+    // log-sum-exp (base 2) per head, from the QK layout of wave 0, shared
+    // through LDS
     if (w == 0 && g == 0) {
 #pragma unroll
         for (int ht = 0; ht < 4; ht++) {
             const int h = 16 * ht + lr;
             const float lsum = ((xchg2[0][h] + xchg2[1][h]) + xchg2[2][h]) + xchg2[3][h];
-            const float lse2 = mq[ht] + __builtin_amdgcn_logf(lsum);   // v_log_f32 is log2
-            if (single) {
-                if (p.lse_out) p.lse_out[b * kHeads + h] = lse2 * kLn2;
-            } else {
-                p.part_lse[((int64_t)b * p.n_chunk + c) * kHeads + h] = lse2;
-            }
+            lse_lds[h] = mq[ht] + __builtin_amdgcn_logf(lsum);   // v_log_f32 is log2
         }
     }
+    __syncthreads();
+
     const int col = 64 * w + lr;
+    // this chunk's normalised output, PV layout
 #pragma unroll
     for (int ht = 0; ht < 4; ht++) {
         const int h0 = 16 * ht + 4 * g;
@@ -505,20 +546,112 @@ void mfa_attn_split_kernel(const AttnArgs p) {
         const f32x4 l3 = *reinterpret_cast<const f32x4*>(&xchg[3][h0]);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int h = h0 + i;
             const float inv = p.v_scale / (((l0[i] + l1[i]) + l2[i]) + l3[i]);
-            if (single) {
-                uint16_t* orow = p.out + ((int64_t)b * kHeads + h) * kHeadDim + col;
 #pragma unroll
-                for (int dt = 0; dt < 4; dt++)
-                    orow[16 * dt] = bitcast<uint16_t>((__bf16)(o[ht][dt][i] * inv));
-            } else {
-                const int64_t pidx = (int64_t)b * p.n_chunk + c;
-                float* prow = p.part_o + (pidx * kHeads + h) * kHeadDim + col;
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++) prow[16 * dt] = o[ht][dt][i] * inv;
-            }
+            for (int dt = 0; dt < 4; dt++) o[ht][dt][i] *= inv;
         }
+    }
+    auto store_final = [&](int h, int dt, float v) {
+        p.out[((int64_t)b * kHeads + h) * kHeadDim + col + 16 * dt] = bitcast<uint16_t>((__bf16)v);
+    };
+    if (single) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ht++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) store_final(16 * ht + 4 * g + i, dt, o[ht][dt][i]);
+        if (p.lse_out && tid < kHeads) p.lse_out[b * kHeads + tid] = lse_lds[tid] * kLn2;
+        return;
+    }
+
+    // several chunks: publish this chunk's partial (normalised output and
+    // base-2 log-sum-exp)
+    const int64_t pidx = (int64_t)b * p.n_chunk + c;
+    const int nc = (L + p.chunk - 1) / p.chunk;
+    if (nc > p.fuse_max) {   // mfa_combine_kernel merges these after this kernel
+#pragma unroll
+        for (int ht = 0; ht < 4; ht++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float* prow = p.part_o + (pidx * kHeads + 16 * ht + 4 * g + i) * kHeadDim + col;
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) prow[16 * dt] = o[ht][dt][i];
+            }
+        if (tid < kHeads) p.part_lse[pidx * kHeads + tid] = lse_lds[tid];
+        return;
+    }
+
+    // few chunks: the workgroup that finishes a sequence's chunks last merges
+    // them. Each workgroup dumps its registers (thread-major: float4 j of
+    // thread tid at (j * 256 + tid), so every instruction writes 4 KB
+    // contiguous) with device-coherent stores that bypass the per-XCD L2;
+    // they are acknowledged (vmcnt 0) before the arrival count. The merging
+    // workgroup reads the other dumps back the same way after seeing the
+    // count. No cache-wide writeback or invalidate is needed.
+    f32x4* dump = reinterpret_cast<f32x4*>(p.part_o) + pidx * (kHeads * kHeadDim / 4);
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int ht = j >> 2, i = j & 3;
+        coherent_store_b128(dump + j * 256 + tid, f32x4{o[ht][0][i], o[ht][1][i], o[ht][2][i], o[ht][3][i]});
+    }
+    if (tid < kHeads)
+        __hip_atomic_store(p.part_lse + pidx * kHeads + tid, lse_lds[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmem<0>();
+    __syncthreads();
+    if (tid == 0) arrival = __hip_atomic_fetch_add(&p.counters[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrival != nc - 1) return;
+    if (tid == 0) __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // chunks in index order whichever workgroup merges, so the result does
+    // not depend on which one finished last
+    const int64_t base = (int64_t)b * p.n_chunk;
+    float M[16], wsum[16];
+    f32x4 acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        M[j] = -__builtin_inff();
+        wsum[j] = 0.f;
+        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int cc = 0; cc < nc; cc++) {
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            const int h = 16 * (j >> 2) + 4 * g + (j & 3);
+            M[j] = fmaxf(M[j], __hip_atomic_load(p.part_lse + (base + cc) * kHeads + h, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT));
+        }
+    }
+    for (int cc = 0; cc < nc; cc++) {
+        f32x4 v[16];
+        if (cc == c) {   // this workgroup's own chunk, still in registers
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const int ht = j >> 2, i = j & 3;
+                v[j] = f32x4{o[ht][0][i], o[ht][1][i], o[ht][2][i], o[ht][3][i]};
+            }
+        } else {
+            const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o) + (base + cc) * (kHeads * kHeadDim / 4);
+            coherent_load_b128x8(v, src + tid, 256);
+            coherent_load_b128x8(v + 8, src + 8 * 256 + tid, 256);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            const int h = 16 * (j >> 2) + 4 * g + (j & 3);
+            const float wc = __builtin_amdgcn_exp2f(
+                __hip_atomic_load(p.part_lse + (base + cc) * kHeads + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M[j]);
+            wsum[j] += wc;
+            acc[j] += wc * v[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int h = 16 * (j >> 2) + 4 * g + (j & 3);
+        const float inv = 1.f / wsum[j];
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) store_final(h, dt, acc[j][dt] * inv);
+        if (p.lse_out && w == 0 && lr == 0) p.lse_out[b * kHeads + h] = (M[j] + __builtin_amdgcn_logf(wsum[j])) * kLn2;
     }
 }
 
@@ -532,7 +665,7 @@ __global__ __launch_bounds__(256) void mfa_combine_kernel(const AttnArgs p) {
     const int d = 4 * (threadIdx.x & 63);
     const int L = seq_len(p.kv, b);
     const int nc = (L + p.chunk - 1) / p.chunk;
-    if (nc <= 1) return;
+    if (nc <= p.fuse_max) return;   // merged by the attention kernel itself
     const int64_t base = (int64_t)b * p.n_chunk;
     float M = -__builtin_inff();
     for (int c = 0; c < nc; c++) M = fmaxf(M, p.part_lse[(base + c) * kHeads + h]);
@@ -572,34 +705,25 @@ __global__ __launch_bounds__(256) void mfa_gather_kernel(const KvView kv, int b,
     }
 }
 
-hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch, hipStream_t st) {
+hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch, const Launch& l) {
     const dim3 grid(batch * a.n_chunk), block(256);
-    if (fp8) {
-        if (paged) hipLaunchKernelGGL((mfa_attn_split_kernel<true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((mfa_attn_split_kernel<true, false>), grid, block, 0, st, a);
-    } else {
-        if (paged) hipLaunchKernelGGL((mfa_attn_split_kernel<false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((mfa_attn_split_kernel<false, false>), grid, block, 0, st, a);
-    }
-    return hipGetLastError();
+    if (fp8)
+        return paged ? launch_kernel(mfa_attn_split_kernel<true, true>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_split_kernel<true, false>, grid, block, l, a);
+    return paged ? launch_kernel(mfa_attn_split_kernel<false, true>, grid, block, l, a)
+                 : launch_kernel(mfa_attn_split_kernel<false, false>, grid, block, l, a);
 }
 
-hipError_t launch_combine(const AttnArgs& a, int batch, hipStream_t st) {
-    hipLaunchKernelGGL(mfa_combine_kernel, dim3(batch * 16), dim3(256), 0, st, a);
-    return hipGetLastError();
+hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l) {
+    return launch_kernel(mfa_combine_kernel, dim3(batch * 16), dim3(256), l, a);
 }
 
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
-                         void* v_dst, hipStream_t st) {
+                         void* v_dst, const Launch& l) {
     const int nblk = (max_seq_len + kStep - 1) / kStep;
     if (nblk == 0) return hipSuccess;
-    if (paged)
-        hipLaunchKernelGGL(mfa_gather_kernel<true>, dim3(nblk), dim3(256), 0, st, kv, b,
-                           (uint8_t*)k_dst, (uint8_t*)v_dst);
-    else
-        hipLaunchKernelGGL(mfa_gather_kernel<false>, dim3(nblk), dim3(256), 0, st, kv, b,
-                           (uint8_t*)k_dst, (uint8_t*)v_dst);
-    return hipGetLastError();
+    return launch_kernel(paged ? mfa_gather_kernel<true> : mfa_gather_kernel<false>, dim3(nblk), dim3(256), l, kv,
+                         b, (uint8_t*)k_dst, (uint8_t*)v_dst);
 }
 
 }  // namespace mfa

@@ -2,12 +2,28 @@
 // kernels (mfa_attn.hip, mfa_qproj.hip). Not installed, not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "mfa_device.h"
 
 namespace mfa {
+
+// Where a kernel goes: the stream and, when timing is on, an event pair that
+// hipExtLaunchKernel stamps with the kernel's own start and end (no marker
+// packets between kernels, so the times match a kernel trace).
+struct Launch {
+    hipStream_t st;
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, const Launch& l,
+                                Args... args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, l.st, l.start, l.stop, 0, args...);
+    return hipGetLastError();
+}
 
 struct AttnArgs {
     const uint16_t* q;      // [B][64][256] bf16
@@ -16,16 +32,24 @@ struct AttnArgs {
     float* lse_out;         // [B][64] or nullptr
     float* part_o;          // workspace [B * n_chunk][64][256] fp32
     float* part_lse;        // workspace [B * n_chunk][64] fp32, base-2
+    int32_t* counters;      // workspace [B] arrival counts, zero between calls
     int32_t chunk;          // tokens per split chunk, multiple of 64
     int32_t n_chunk;        // chunks per sequence slot in the launch = ceil(max_seq_len / chunk)
+    int32_t fuse_max;       // sequences with 2..fuse_max chunks are merged in the attention kernel
     float score_scale;      // softmax_scale * k_scale * log2(e)
     float v_scale;          // 1 for bf16
 };
 
-hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch, hipStream_t st);
-hipError_t launch_combine(const AttnArgs& a, int batch, hipStream_t st);
+// Launches whose sequences all have at most this many chunks merge them
+// inside the attention kernel (the last chunk to finish does it); other
+// launches run mfa_combine_kernel afterwards. With more chunks the serial
+// merge at the tail costs more than the second launch.
+constexpr int kFusedMaxChunks = 2;
+
+hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch, const Launch& l);
+hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l);
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
-                         void* v_dst, hipStream_t st);
+                         void* v_dst, const Launch& l);
 
 struct QprojArgs {
     const uint16_t* x;      // [B][hidden]
@@ -41,8 +65,8 @@ struct QprojArgs {
 
 constexpr int kQprojSplit = 8;   // K-splits of the down-projection
 
-hipError_t launch_qproj_down(const QprojArgs& a, hipStream_t st);
-hipError_t launch_rmsnorm(const QprojArgs& a, hipStream_t st);
-hipError_t launch_qproj_up(const QprojArgs& a, hipStream_t st);
+hipError_t launch_qproj_down(const QprojArgs& a, const Launch& l);
+hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l);
+hipError_t launch_qproj_up(const QprojArgs& a, const Launch& l);
 
 }  // namespace mfa

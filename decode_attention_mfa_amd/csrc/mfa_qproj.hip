@@ -133,24 +133,21 @@ __global__ __launch_bounds__(256) void mfa_rmsnorm_kernel(const float* __restric
     }
 }
 
-hipError_t launch_qproj_down(const QprojArgs& a, hipStream_t st) {
+hipError_t launch_qproj_down(const QprojArgs& a, const Launch& l) {
     const int mblk = (a.batch + 63) / 64;
-    hipLaunchKernelGGL(mfa_skinny_gemm_kernel<false>, dim3(a.rank / 64, a.ksplit, mblk), dim3(256), 0, st,
-                       a.x, a.hidden, a.w_qa, a.rank, a.hidden, a.batch, (void*)a.c_part);
-    return hipGetLastError();
+    return launch_kernel(mfa_skinny_gemm_kernel<false>, dim3(a.rank / 64, a.ksplit, mblk), dim3(256), l, a.x,
+                         a.hidden, a.w_qa, a.rank, a.hidden, a.batch, (void*)a.c_part);
 }
 
-hipError_t launch_rmsnorm(const QprojArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(mfa_rmsnorm_kernel, dim3(a.batch), dim3(256), 0, st, a.c_part, a.ksplit, a.batch,
-                       a.rank, a.rms_w, a.eps, a.chat);
-    return hipGetLastError();
+hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l) {
+    return launch_kernel(mfa_rmsnorm_kernel, dim3(a.batch), dim3(256), l, (const float*)a.c_part, a.ksplit, a.batch,
+                         a.rank, a.rms_w, a.eps, a.chat);
 }
 
-hipError_t launch_qproj_up(const QprojArgs& a, hipStream_t st) {
+hipError_t launch_qproj_up(const QprojArgs& a, const Launch& l) {
     const int mblk = (a.batch + 63) / 64;
-    hipLaunchKernelGGL(mfa_skinny_gemm_kernel<true>, dim3(a.nq / 64, 1, mblk), dim3(256), 0, st,
-                       a.chat, a.rank, a.w_qb, a.nq, a.rank, a.batch, (void*)a.q_out);
-    return hipGetLastError();
+    return launch_kernel(mfa_skinny_gemm_kernel<true>, dim3(a.nq / 64, 1, mblk), dim3(256), l,
+                         (const uint16_t*)a.chat, a.rank, a.w_qb, a.nq, a.rank, a.batch, (void*)a.q_out);
 }
 
 }  // namespace mfa

@@ -96,8 +96,9 @@ typedef struct {
  * allocates the split-K workspace on the current device:
  *   max_batch * ceil(max_context / C) * 64 * (256 + 1) * 4 bytes of chunk
  *   partials, C = split_tokens or, when that is 0, 256 (the smallest chunk
- *   chosen per call), plus Q-projection scratch of max_batch * q_rank * 34
- *   bytes.
+ *   chosen per call), max_batch 4-byte arrival counters (zeroed here, left
+ *   at zero by every call), plus Q-projection scratch of
+ *   max_batch * q_rank * 34 bytes.
  * On success stores the handle in *out (host pointer) and returns MFA_OK. */
 int mfa_create(const mfa_config* cfg, mfa_handle* out);
 
@@ -122,7 +123,10 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
  * fp32 or NULL. L_b = 0 gives out = 0 and lse = -inf.
  * The KV range of each sequence is cut into chunks of split_tokens tokens
  * (or a per-call choice when split_tokens is 0); chunk partials go to the
- * handle's workspace and are merged by the log-sum-exp identity. The result
+ * handle's workspace and are merged by the log-sum-exp identity, in chunk
+ * order: inside the attention kernel by the last chunk to finish when no
+ * sequence of the call has more than two chunks, else by a second kernel on
+ * the same stream. The result
  * depends only on the logical K/V values and the chunking, not on the cache
  * layout: paged and contiguous caches holding the same rows give bitwise
  * equal outputs. 1 <= batch <= max_batch. */

@@ -62,7 +62,7 @@ def test_tiny_config():
     check_parity(synth.config_case(1), label="tiny B=1 L=256 bf16")
 
 
-@pytest.mark.parametrize("split", [0, 64, 192, 1024, 4096])
+@pytest.mark.parametrize("split", [0, 64, 192, 512, 704, 1024, 4096])
 def test_fp8_contiguous_splits(split):
     check_parity(synth.config_case(3, batch=3, scale_len=0.5), split_tokens=split,
                  label=f"fp8 contiguous B=3 L=2048 split={split}")
@@ -223,3 +223,43 @@ def test_dominant_late_keys_restart(kv):
                           q=case.q, k_scale=ks, v_scale=vs)
     for split in (0, 512):
         check_parity(case, split_tokens=split, label=f"dominant late keys {kv} split={split}")
+
+
+@pytest.mark.parametrize("split", [1024, 256])
+def test_graph_replay_matches_eager(split):
+    """mfa_decode captured into a HIP graph (through torch's capture on a side
+    stream), replayed several times with other eager decodes in between: every
+    replay equals the eager result bitwise. split 1024 merges the two chunks in
+    the attention kernel, 256 uses the combine kernel."""
+    m, hz = _mfa()
+    case = synth.config_case(3, batch=3, scale_len=0.5)
+    other = synth.config_case(3, batch=3, scale_len=0.5, q_std=2.0)
+    dc, do = hz.to_device(case), hz.to_device(other)
+    h = hz.create_handle(dc, split_tokens=split)
+    try:
+        st = torch.cuda.Stream()
+        out, lse = hz.alloc_outputs(dc)
+        oo, lo = hz.alloc_outputs(do)
+        kv, kvo = dc.kv(), do.kv()
+        with torch.cuda.stream(st):
+            m.mfa_decode(h, dc.q, kv, out, lse, dc.batch, st)
+        torch.cuda.synchronize()
+        ref_o, ref_l = out.clone(), lse.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            m.mfa_decode(h, dc.q, kv, out, lse, dc.batch, st)
+        for r in range(4):
+            _say(f"[graph] split={split} replay {r}")
+            out.zero_()
+            lse.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+            with torch.cuda.stream(st):
+                m.mfa_decode(h, do.q, kvo, oo, lo, do.batch, st)
+            torch.cuda.synchronize()
+        o_ref, _ = oracle.case_attention(case)
+        assert row_err(hz.bf16_to_f64(out), o_ref) <= TOL
+    finally:
+        m.mfa_destroy(h)
