@@ -42,7 +42,10 @@ DESCRIPTION = {
     "paged_ragged": "B=384, L~U[1024,8192], FP8-E4M3 KV, 64-token pages, permuted page table, decode only",
     "long_splitk": "B=8, L=32768 x4 + 65536 x4, bf16 KV, split-K 512-token chunks, decode only",
 }
-ATTN_SOURCES = ("decode_attention_mfa_amd/csrc/mfa_attn.hip", "decode_attention_mfa_amd/csrc/mfa_device.h")
+# sources that decide the attention kernel's memory traffic (kernel, launch
+# shape, split and merge policy); the stored HBM counters hold for this hash
+ATTN_SOURCES = ("decode_attention_mfa_amd/csrc/mfa_attn.hip", "decode_attention_mfa_amd/csrc/mfa_device.h",
+                "decode_attention_mfa_amd/csrc/mfa_internal.h", "decode_attention_mfa_amd/csrc/mfa_api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WARMUP_SECONDS = 0.5
 
@@ -59,11 +62,14 @@ def attn_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(case):
+def algorithmic_bytes(case, attention_writes_out: bool):
     """(attention-kernel bytes, whole-step bytes) the method must move.
-    Attention: every cached K and V row t < L_b, Q, the lengths and (paged)
-    the page-table entries it reads. Step: that plus the bf16 output and, for
-    the full layer, x, gamma and both projection weights."""
+    Attention: every cached K and V row t < L_b (512 B per token with FP8,
+    1024 B with bf16), Q (32 KB per sequence), the lengths and (paged) the
+    page-table entries it reads, and the bf16 output (32 KB per sequence)
+    when the attention kernel writes it (no separate merge launch). Step:
+    all of that plus the output, and for the full layer x, gamma and both
+    projection weights (Q is then produced on the device, not read)."""
     import numpy as np
     B = case.batch
     kv = case.kv_bytes_read()
@@ -72,11 +78,11 @@ def algorithmic_bytes(case):
     meta = B * 4
     if case.paged:
         meta += int(((case.seq_lens.astype(np.int64) + 63) // 64).sum()) * 4
-    attn = kv + q + meta
-    step = attn + o
+    attn = kv + q + meta + (o if attention_writes_out else 0)
+    step = kv + q + meta + o
     if case.x is not None:
         step += case.x.nbytes + case.w_qa.nbytes + case.w_qb.nbytes + case.gamma.nbytes
-        attn -= q          # Q is produced on the device, not an input of the step
+        attn -= q
         step -= q
     return attn, step
 
@@ -169,7 +175,7 @@ def main():
     t0 = time.perf_counter()
     case = synth.config_case(WORKLOADS[wl])
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s")
-    attn_bytes, step_bytes = algorithmic_bytes(case)
+    _, step_bytes = algorithmic_bytes(case, True)
 
     dc = harness.to_device(case)
     # rotate copies of the per-step inputs so that no step finds them in the MALL
@@ -234,6 +240,7 @@ def main():
 
     ms_per_step = dt * 1e3 / args.steps
     value = dc.batch / (ms_per_step / 1e3)
+    attn_bytes, _ = algorithmic_bytes(case, prof["combine"][0] == 0)
     n_attn, ms_attn = prof["attention"]
     attn_ms = ms_attn / max(n_attn, 1)
     achieved = attn_bytes / (attn_ms / 1e3) / 1e9

@@ -7,24 +7,30 @@
 //
 // One workgroup (4 wave64s) owns one (sequence, chunk). It walks the chunk in
 // steps of 64 tokens (= one cache page):
-//   QK   wave w scores tokens 16w..16w+15 of the step against all 64 heads:
-//        S^T[16 tok x 64 heads] = K[16 x 256] . Q^T, the K rows going straight
-//        from HBM into MFMA A-operand registers (FP8 codes converted to bf16
-//        in registers; E4M3 values are exact in bf16), Q held in registers as
-//        B operands for the whole chunk. Each cached K byte feeds 64 heads.
-//   max  per-head step maxima meet in LDS; every wave derives the same new
-//        running max, so all rows of P share one reference.
-//   P    exp2 of the scaled scores, rounded to bf16, written to LDS.
-//   PV   wave w owns output columns 64w..64w+63 of all 64 heads:
-//        O[64 x 64] += P[64 x 64 tok] . V[64 tok x 64]; its V slice goes
-//        HBM -> registers -> LDS and comes back transposed with
-//        ds_read_b64_tr_b8 / _b16 as the MFMA B operand.
-// The next step's K and V are loaded while the current step computes.
+//   load  K and V rows of a step go from HBM straight into an LDS ring slot
+//         (global_load_lds_dwordx4, no registers); FP8 keeps 4 steps in
+//         flight, bf16 2. Wave w fetches rows 16w..16w+15 of both tensors.
+//   QK    wave w scores its 16 tokens against all 64 heads:
+//         S^T[16 tok x 64 heads] = K[16 x 256] . Q^T with bf16 MFMA 16x16x32,
+//         K rows from LDS as A operands (FP8 codes widened to bf16 in
+//         registers; every E4M3 value is exact in bf16), Q held in registers
+//         as B operands for the whole chunk. Each cached K byte feeds 64 heads.
+//   P     exp2 of the scaled scores against per-head reference maxima that
+//         stay fixed for a pass over the chunk (the exact maxima of its first
+//         step), rounded to bf16 into LDS. A score above its reference by more
+//         than kTau (base 2) makes the waves vote to redo the chunk with a
+//         higher reference, so the output is never rescaled inside the loop.
+//   PV    wave w owns output columns 64w..64w+63 of all 64 heads:
+//         O[64 x 64] += P[64 x 64 tok] . V[64 tok x 64], V read transposed
+//         from the shared tile with ds_read_b64_tr_b8 / _b16.
+// One workgroup barrier per step orders the ring, P and the vote.
 //
 // Scores are kept in the base-2 domain: s2 = s * log2(e), exp -> exp2.
-// Output of a chunk: if the sequence has one chunk, the final bf16 output and
-// lse; otherwise the chunk-normalised output (fp32) and its base-2 lse in the
-// workspace, merged by mfa_combine_kernel.
+// Output of a chunk: for a one-chunk sequence the final bf16 output and lse;
+// otherwise the chunk-normalised output (fp32) and its base-2 lse, merged by
+// the log-sum-exp identity either here, by the last of the sequence's chunks
+// to finish (launches where no sequence has more than two chunks), or by
+// mfa_combine_kernel afterwards.
 #include <type_traits>
 
 #include "mfa_device.h"
