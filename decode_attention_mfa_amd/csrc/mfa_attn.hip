@@ -81,7 +81,7 @@ __device__ __forceinline__ void lds_barrier() {
 // order the reads instead. No register is written, and the "memory" clobber
 // keeps earlier reads of the slot ahead of it.
 __device__ __forceinline__ void dma_b128(const void* sbase, uint32_t voff, uint32_t lds_dst) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_dst) : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds_dst) : "memory");
 }
 
 // A pointer every lane of the wave holds, moved to scalar registers.
