@@ -137,6 +137,9 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     if (c.split_tokens < 0 || c.split_tokens % mfa::kStep != 0)
         return fail(MFA_ERR_INVALID, "mfa_create: split_tokens must be 0 or a positive multiple of 64 (got %d)",
                     c.split_tokens);
+    if (c.page_size != 0 && c.split_tokens > mfa::kMaxPagedChunkSteps * mfa::kStep)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: with a paged cache split_tokens must be <= %d (got %d)",
+                    mfa::kMaxPagedChunkSteps * mfa::kStep, c.split_tokens);
     if (!(c.softmax_scale > 0.f) || !isfinite(c.softmax_scale))
         return fail(MFA_ERR_INVALID, "mfa_create: softmax_scale must be finite and > 0");
     if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))

@@ -191,12 +191,33 @@ void mfa_attn_split_kernel(const AttnArgs p) {
         voff[i] = r * ROWB + 16 * ((l % CPR) ^ vswz<FP8>(r));
     }
 
+    // ---- paged caches: the pages of the chunk's steps, fetched once. Lane j
+    // holds the page of step j (pg0) and of step 64 + j (pg1); a step reads
+    // its page with v_readlane, so no load (and no wait for one) sits in the
+    // loop. Paged chunks have at most kMaxPagedChunkSteps = 128 steps (the
+    // host enforces it).
+    int32_t pg0 = 0, pg1 = 0;
+    if constexpr (PAGED) {
+        const int32_t* chunk_pt = p.kv.page_table + (int64_t)b * p.kv.pt_stride + (t_begin >> 6);
+        if (l < nsteps) pg0 = chunk_pt[l];
+        if (64 + l < nsteps) pg1 = chunk_pt[64 + l];
+    }
+    // first cache row of step s (s <= last_s)
+    auto step_row = [&](int s) -> int64_t {
+        if constexpr (PAGED) {
+            const int32_t page = s < 64 ? __builtin_amdgcn_readlane(pg0, s) : __builtin_amdgcn_readlane(pg1, s - 64);
+            return (int64_t)page * kPage;
+        } else {
+            return kv_step_base<false>(p.kv, b, t_begin + s * kStep);
+        }
+    };
+
     // ---- issue the loads of step s (clamped to the last step, whose rows then
     // hit in L2) into ring slot s % RING: this wave's 16 K rows into its
     // private region, and the same 16 rows of V into the shared V tile.
     auto issue_step = [&](int s) {
         const int t0 = t_begin + min(s, last_s) * kStep;
-        const int64_t base = kv_step_base<PAGED>(p.kv, b, t0);
+        const int64_t base = step_row(min(s, last_s));
         const uint8_t* kb = wave_uniform(p.kv.k + base * ROWB);
         const uint8_t* vb = wave_uniform(p.kv.v + base * ROWB);
         const int slot = s % RING;
@@ -220,30 +241,31 @@ void mfa_attn_split_kernel(const AttnArgs p) {
         }
     };
 
-    // The ring's first steps stream in while Q is fetched.
+    // ---- Q, fetched once per workgroup by DMA into the staging area (slot
+    // RING-1 of the ring, free until the first step's barrier): 16-byte
+    // chunk c of head h at position c ^ (h & 15); wave w copies heads
+    // 16w..16w+15. The ring's first steps stream in behind it.
+    uint8_t* const qs = smem + (RING - 1) * SLOT;
+    {
+        const uint8_t* qb = wave_uniform(reinterpret_cast<const uint8_t*>(p.q + (int64_t)b * kHeads * kHeadDim));
+        const uint32_t qd = __builtin_amdgcn_readfirstlane(lds_addr(qs + 16 * w * 512));
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int h = 16 * w + 2 * i + (l >> 5);
+            dma_b128(qb, (uint32_t)(h * 512 + 16 * ((l & 31) ^ (h & 15))), qd + 1024 * i);
+        }
+    }
 #pragma unroll
     for (int s = 0; s < RING - 1; s++) issue_step(s);
 
-    // ---- Q, fetched once per workgroup: wave w copies heads 16w..16w+15 into
-    // the staging area (16-byte chunk c of head h at position c ^ (h & 15)),
-    // then every wave reads its B operands: qop[ht][ks] holds
-    // Q[16ht + lr][d(ks, g, 0..7)] with d(ks, g, j) = 64*(ks/2) + 16*g +
-    // 8*(ks%2) + j, the same d order the K A operands use below.
+    // Every wave reads its B operands: qop[ht][ks] holds Q[16ht + lr][d(ks,
+    // g, 0..7)] with d(ks, g, j) = 64*(ks/2) + 16*g + 8*(ks%2) + j, the same
+    // d order the K A operands use below.
     bf16x8 qop[4][8];
     {
-        uint8_t* qs = smem + (RING - 1) * SLOT;
-        const uint16_t* qb = p.q + (int64_t)b * kHeads * kHeadDim;
-        u32x4 qv[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int h = 16 * w + 2 * i + (l >> 5);
-            qv[i] = *reinterpret_cast<const u32x4*>(qb + h * kHeadDim + 8 * (l & 31));
-        }
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int h = 16 * w + 2 * i + (l >> 5);
-            lds_store_b128(qs + h * 512 + 16 * ((l & 31) ^ (h & 15)), qv[i]);
-        }
+        // this wave's Q rows have landed once at most the ring's loads are in
+        // flight; the barrier makes every wave's rows visible
+        wait_vmem<(RING - 1) * OPS>();
         lds_barrier();
 #pragma unroll
         for (int ht = 0; ht < 4; ht++)

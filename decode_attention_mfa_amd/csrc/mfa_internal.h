@@ -46,6 +46,10 @@ struct AttnArgs {
 // merge at the tail costs more than the second launch.
 constexpr int kFusedMaxChunks = 2;
 
+// Paged caches: at most this many 64-token steps per split chunk (the
+// attention kernel keeps a chunk's page indices in two registers per lane).
+constexpr int kMaxPagedChunkSteps = 128;
+
 hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch, const Launch& l);
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l);
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,

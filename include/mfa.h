@@ -64,7 +64,8 @@ typedef struct {
     int32_t page_size;     /* 0 = contiguous cache; otherwise must be 64 */
     int32_t max_batch;     /* largest batch any call will pass, >= 1 */
     int32_t max_context;   /* largest sequence length any call will pass, >= 1 */
-    int32_t split_tokens;  /* split-K chunk in tokens, multiple of 64; 0 = chosen per call */
+    int32_t split_tokens;  /* split-K chunk in tokens, multiple of 64; 0 = chosen per call;
+                              at most 8192 with a paged cache (else MFA_ERR_UNSUPPORTED) */
     float rms_eps;         /* RMSNorm epsilon (1e-6), >= 0 */
     float softmax_scale;   /* score scale (1/16 = 1/sqrt(256)), finite and > 0 */
 } mfa_config;
