@@ -686,31 +686,59 @@ void mfa_attn_split_kernel(const AttnArgs p) {
 // Merge the chunk partials of every sequence with more than one chunk:
 //   M = max_c lse2_c, W_c = 2^(lse2_c - M), out = sum_c W_c o_c / sum_c W_c,
 //   lse = (M + log2 sum_c W_c) * ln 2.
-// Block (b, head quad); thread -> head 4*hq + tid/64, columns 4*(tid%64)..+3.
-__global__ __launch_bounds__(256) void mfa_combine_kernel(const AttnArgs p) {
-    const int b = blockIdx.x >> 4;
-    const int h = 4 * (blockIdx.x & 15) + (threadIdx.x >> 6);
-    const int d = 4 * (threadIdx.x & 63);
+// One wave per (sequence, head); lane t owns columns 4t..4t+3. The chunk
+// weights go through LDS; the partial rows (1 KB per chunk, contiguous) are
+// read kCombineUnroll at a time so that many loads are in flight. Chunks are
+// accumulated in index order.
+constexpr int kCombineUnroll = 16;
+constexpr int kCombineBlock = 1024;   // chunk weights staged per round
+__global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
+    __shared__ float wts[kCombineBlock];
+    const int b = blockIdx.x >> 6;
+    const int h = blockIdx.x & 63;
+    const int t = threadIdx.x;
     const int L = seq_len(p.kv, b);
     const int nc = (L + p.chunk - 1) / p.chunk;
     if (nc <= p.fuse_max) return;   // merged by the attention kernel itself
     const int64_t base = (int64_t)b * p.n_chunk;
+    const float* lse = p.part_lse + base * kHeads + h;   // chunk c at lse[c * kHeads]
+    constexpr int64_t kRow = kHeads * kHeadDim / 4;      // f32x4 per chunk partial
+    const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + (base * kHeads + h) * (kHeadDim / 4) + t;
+
     float M = -__builtin_inff();
-    for (int c = 0; c < nc; c++) M = fmaxf(M, p.part_lse[(base + c) * kHeads + h]);
-    float sum = 0.f;
+    for (int c = t; c < nc; c += 64) M = fmaxf(M, lse[(int64_t)c * kHeads]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+    float wpart = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nc; c++) {
-        const float wgt = __builtin_amdgcn_exp2f(p.part_lse[(base + c) * kHeads + h] - M);
-        const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_o + ((base + c) * kHeads + h) * kHeadDim + d);
-        sum += wgt;
-        acc += wgt * v;
+    for (int c0 = 0; c0 < nc; c0 += kCombineBlock) {
+        const int n = min(kCombineBlock, nc - c0);
+        for (int i = t; i < n; i += 64) {
+            const float wv = __builtin_amdgcn_exp2f(lse[(int64_t)(c0 + i) * kHeads] - M);
+            wts[i] = wv;
+            wpart += wv;
+        }
+        __syncthreads();
+        int i = 0;
+        for (; i + kCombineUnroll <= n; i += kCombineUnroll) {
+            f32x4 v[kCombineUnroll];
+#pragma unroll
+            for (int j = 0; j < kCombineUnroll; j++) v[j] = po[(int64_t)(c0 + i + j) * kRow];
+#pragma unroll
+            for (int j = 0; j < kCombineUnroll; j++) acc += wts[i + j] * v[j];
+        }
+        for (; i < n; i++) acc += wts[i] * po[(int64_t)(c0 + i) * kRow];
+        __syncthreads();
     }
-    const float inv = 1.f / sum;
-    uint16_t* orow = p.out + ((int64_t)b * kHeads + h) * kHeadDim + d;
+    float wsum = wpart;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
+    const float inv = 1.f / wsum;
+    uint16_t* orow = p.out + ((int64_t)b * kHeads + h) * kHeadDim + 4 * t;
     *reinterpret_cast<u32x2*>(orow) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
                                            pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-    if (p.lse_out && (threadIdx.x & 63) == 0)
-        p.lse_out[b * kHeads + h] = (M + __builtin_amdgcn_logf(sum)) * kLn2;
+    if (p.lse_out && t == 0) p.lse_out[b * kHeads + h] = (M + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
 // Copy the logical rows t < L_b of sequence b through the attention kernel's
@@ -743,7 +771,7 @@ hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch,
 }
 
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l) {
-    return launch_kernel(mfa_combine_kernel, dim3(batch * 16), dim3(256), l, a);
+    return launch_kernel(mfa_combine_kernel, dim3(batch * kHeads), dim3(64), l, a);
 }
 
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
