@@ -55,7 +55,7 @@ struct mfa_ctx {
     float* part_o;         // [max_batch * max_chunks][64][256]
     float* part_lse;       // [max_batch * max_chunks][64]
     int32_t* counters;     // [max_batch], zero between calls
-    float* c_part;         // [kQprojSplit][max_batch][q_rank]
+    float* c_part;         // [hidden / kQprojRowsPerSplit][max_batch][q_rank]
     uint16_t* chat;        // [max_batch][q_rank]
 };
 
@@ -122,9 +122,9 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     if (c.num_heads != mfa::kHeads || c.head_dim != mfa::kHeadDim)
         return fail(MFA_ERR_UNSUPPORTED, "mfa_create: only 64 heads x 256 are supported (got %d x %d)",
                     c.num_heads, c.head_dim);
-    if (c.hidden <= 0 || c.hidden % (64 * mfa::kQprojSplit) != 0)
+    if (c.hidden <= 0 || c.hidden % mfa::kQprojRowsPerSplit != 0)
         return fail(MFA_ERR_UNSUPPORTED, "mfa_create: hidden must be a positive multiple of %d (got %d)",
-                    64 * mfa::kQprojSplit, c.hidden);
+                    mfa::kQprojRowsPerSplit, c.hidden);
     if (c.q_rank <= 0 || c.q_rank % 64 != 0 || c.q_rank > 65536)
         return fail(MFA_ERR_UNSUPPORTED, "mfa_create: q_rank must be a positive multiple of 64 (got %d)",
                     c.q_rank);
@@ -150,7 +150,7 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     const int64_t nparts = (int64_t)c.max_batch * max_chunks;
     const int64_t bytes_o = nparts * mfa::kHeads * mfa::kHeadDim * 4;
     const int64_t bytes_lse = nparts * mfa::kHeads * 4;
-    const int64_t bytes_c = (int64_t)mfa::kQprojSplit * c.max_batch * c.q_rank * 4;
+    const int64_t bytes_c = (int64_t)(c.hidden / mfa::kQprojRowsPerSplit) * c.max_batch * c.q_rank * 4;
     const int64_t bytes_chat = (int64_t)c.max_batch * c.q_rank * 2;
     if (max_chunks > (1 << 24) || nparts > (int64_t)1 << 31)
         return fail(MFA_ERR_INVALID, "mfa_create: max_batch * max_context too large");
@@ -235,7 +235,7 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w, 
     a.hidden = h->cfg.hidden;
     a.rank = h->cfg.q_rank;
     a.nq = mfa::kHeads * mfa::kHeadDim;
-    a.ksplit = mfa::kQprojSplit;
+    a.ksplit = a.hidden / mfa::kQprojRowsPerSplit;
     a.eps = h->cfg.rms_eps;
     hipStream_t st = (hipStream_t)hip_stream;
     hipError_t e = timed_launch(h, MFA_KERNEL_QPROJ_DOWN, st, [&](const mfa::Launch& l) { return mfa::launch_qproj_down(a, l); });

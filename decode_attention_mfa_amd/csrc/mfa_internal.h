@@ -67,7 +67,10 @@ struct QprojArgs {
     float eps;
 };
 
-constexpr int kQprojSplit = 8;   // K-splits of the down-projection
+// The down-projection splits K into blocks of this many rows (one
+// workgroup each, fp32 partials summed by the RMSNorm kernel); hidden must be
+// a multiple of it.
+constexpr int kQprojRowsPerSplit = 512;
 
 hipError_t launch_qproj_down(const QprojArgs& a, const Launch& l);
 hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l);

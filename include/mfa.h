@@ -99,7 +99,7 @@ typedef struct {
  *   partials, C = split_tokens or, when that is 0, 256 (the smallest chunk
  *   chosen per call), max_batch 4-byte arrival counters (zeroed here, left
  *   at zero by every call), plus Q-projection scratch of
- *   max_batch * q_rank * 34 bytes.
+ *   max_batch * q_rank * (4 * hidden / 512 + 2) bytes.
  * On success stores the handle in *out (host pointer) and returns MFA_OK. */
 int mfa_create(const mfa_config* cfg, mfa_handle* out);
 
