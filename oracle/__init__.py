@@ -68,6 +68,16 @@ def _load():
         lib.oracle_weights.restype = I
         lib.oracle_gather_kv.argtypes = [I, I, I, P, P, P, P, I, I, I64, P, P]
         lib.oracle_gather_kv.restype = I
+        lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+        lib.oracle_encode_bf16.argtypes = [P, P, I64]
+        lib.oracle_encode_e4m3.argtypes = [P, P, I64]
+        lib.oracle_kv_project.argtypes = [I, I, I, P, P, P, P, P, I]
+        lib.oracle_kv_project.restype = I
+        lib.oracle_kv_append.argtypes = [I, I, I, P, P, D, D, P, P, P, P, I, I, I64, I]
+        lib.oracle_kv_append.restype = I
         _lib = lib
         return lib
 
@@ -102,6 +112,62 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     out = np.empty(codes.shape, dtype=np.float64)
     _load().oracle_decode_e4m3(_ptr(codes), _ptr(out), codes.size)
     return out
+
+
+def encode_bf16(x) -> np.ndarray:
+    """float32 values -> bf16 bits, round to nearest even."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_encode_bf16(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def encode_e4m3(x) -> np.ndarray:
+    """float32 values -> E4M3FN codes, round to nearest even, saturating at 448."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().oracle_encode_e4m3(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def kv_project(x, w_k, w_v, nthreads: int = 0):
+    """x [B, hidden], w_k and w_v [hidden, D] as bf16 bits -> (k, v) [B, D] fp64."""
+    x, w_k, w_v = (_c(a, np.uint16) for a in (x, w_k, w_v))
+    B, hidden = x.shape
+    D = w_k.shape[1]
+    assert w_k.shape == (hidden, D) and w_v.shape == (hidden, D)
+    k = np.empty((B, D), dtype=np.float64)
+    v = np.empty((B, D), dtype=np.float64)
+    rc = _load().oracle_kv_project(B, hidden, D, _ptr(x), _ptr(w_k), _ptr(w_v), _ptr(k), _ptr(v),
+                                   nthreads)
+    if rc:
+        raise RuntimeError(f"oracle_kv_project failed: {rc}")
+    return k, v
+
+
+def kv_append(k_new, v_new, k, v, seq_lens, *, kv_dtype: int, k_scale: float = 1.0,
+              v_scale: float = 1.0, page_table=None, page_size: int = 64) -> int:
+    """Write the encoded rows k_new, v_new [B, D] (fp64) into the caches k, v
+    (raw bits, modified in place: contiguous [B, S, D] or paged [P, page, D])
+    at row seq_lens[b]. Returns the number of sequences written."""
+    k_new = _c(k_new, np.float64)
+    v_new = _c(v_new, np.float64)
+    B, D = k_new.shape
+    raw = np.uint16 if kv_dtype == KV_BF16 else np.uint8
+    for a in (k, v):
+        assert a.dtype == raw and a.flags.c_contiguous and a.shape[-1] == D
+    L = _c(seq_lens, np.int32)
+    assert L.shape == (B,)
+    if page_table is not None:
+        pt = _c(page_table, np.int32)
+        pt_stride, kv_stride, num_pages = pt.shape[1], 0, k.shape[0]
+        assert k.shape[1] == page_size
+    else:
+        pt, pt_stride, kv_stride, num_pages = None, 0, k.shape[1], 0
+        assert k.shape[0] == B
+    return int(_load().oracle_kv_append(B, D, kv_dtype, _ptr(k_new), _ptr(v_new), float(k_scale),
+                                        float(v_scale), _ptr(k), _ptr(v), _ptr(L), _ptr(pt),
+                                        pt_stride, page_size, kv_stride, num_pages))
 
 
 def qproj(x, w_qa, gamma, w_qb, eps: float = 1e-6, nthreads: int = 0, return_c: bool = False):

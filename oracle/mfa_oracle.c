@@ -27,7 +27,10 @@
  *     token t, at row t % page_size (PagedAttention, cited by title);
  *   - split-K (Flash-Decoding, cited by title on the DeepSeek-V4 page): chunks
  *     of `chunk` tokens from token 0, each reduced to (max, sum, normalised
- *     output), merged by the log-sum-exp identity.
+ *     output), merged by the log-sum-exp identity;
+ *   - the new token's K and V rows are x . W_k and x . W_v (hidden -> 256),
+ *     rounded to float, divided by the tensor's scale for FP8, encoded by
+ *     round-to-nearest-even (E4M3 saturating at +-448) and written at row L_b.
  *
  * Every floating-point step runs in IEEE double. Inputs in bf16 / E4M3 are
  * decoded exactly (both formats are subsets of double).
@@ -38,7 +41,11 @@
  * 50-digit decimal brute force on tiny inputs, numpy dgemm for the
  * projections, RMSNorm scale invariance and closed form, the 256-code E4M3
  * table against the OCP closed form and torch.float8_e4m3fn, paged equals
- * contiguous bit for bit, split equals unsplit.
+ * contiguous bit for bit, split equals unsplit; for the append: the encoders
+ * against torch and against exact midpoints between neighbouring codes (ties
+ * to even), saturation, the K/V projection against numpy dgemm and decimal
+ * brute force, and the append touching exactly row L_b (paged and contiguous
+ * agreeing).
  */
 #include <math.h>
 #include <stdint.h>
@@ -399,4 +406,134 @@ int oracle_gather_kv(int b, int D, int elem_bytes, const void* k, const void* v,
         memcpy((char*)v_dst + (size_t)t * rb, (const char*)v + (size_t)row * rb, rb);
     }
     return L;
+}
+
+/* ---------------------------------------------------------------- KV append */
+/*
+ * The step before attention in a decode layer: the new token's key and value
+ * from its hidden state, k = x . W_k and v = x . W_v (hidden -> D each, one
+ * shared K head and one shared V head: Step-3 summary card, Key points),
+ * written at row L_b of sequence b (paged: page page_table[b][L_b / 64], row
+ * L_b % 64, as in PagedAttention). The cache stores bf16, or E4M3 of the
+ * value divided by the tensor's scale.
+ *
+ * The rounding to the cache format is an integer decision taken from a
+ * floating-point value: it is taken here from the value rounded to float
+ * (and divided by the scale in float), the precision the GPU computes in.
+ */
+
+/* bf16 bits of a float by round-to-nearest-even; NaN stays a quiet NaN. */
+uint16_t oracle_f32_to_bf16(float x) {
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7fffu + lsb) >> 16);
+}
+
+/* OCP E4M3FN code of a float by round-to-nearest-even. Finite values beyond
+ * the largest code (448) saturate to +-448 (the format has no infinities);
+ * NaN gives 0x7f with the sign. Written from the format's definition: value
+ * = 2^(e-7) * (1 + m/8) for exponent field e >= 1, 2^-6 * m/8 for e = 0. */
+uint8_t oracle_f32_to_e4m3(float x) {
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs((double)x);
+    if (isnan(x))
+        return sign | 0x7f;
+    if (a >= 448.0)
+        return sign | 0x7e;
+    if (a < 0.015625) {                 /* below 2^-6: multiples of 2^-9 */
+        double u = a * 512.0;           /* exact */
+        double r = nearbyint(u);        /* ties to even (default rounding mode) */
+        return sign | (uint8_t)r;       /* 8 is the smallest normal, code 0x08 */
+    }
+    int e2;
+    double f = frexp(a, &e2);           /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                     /* a = (2f) * 2^e, 2f in [1, 2) */
+    double m = (2.0 * f - 1.0) * 8.0;   /* exact: a float has 24 bits */
+    double q = nearbyint(m);
+    if (q == 8.0) {
+        q = 0.0;
+        e += 1;
+    }
+    int code = ((e + 7) << 3) | (int)q;
+    if (code > 0x7e)
+        code = 0x7e;
+    return sign | (uint8_t)code;
+}
+
+void oracle_encode_bf16(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f32_to_bf16(in[i]);
+}
+
+void oracle_encode_e4m3(const float* in, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_f32_to_e4m3(in[i]);
+}
+
+/* k_out, v_out [B][D] = x [B][hidden] . W_k, W_v [hidden][D] (bf16 inputs),
+ * summed in fp64. */
+int oracle_kv_project(int B, int hidden, int D, const uint16_t* x, const uint16_t* w_k,
+                      const uint16_t* w_v, double* k_out, double* v_out, int nthreads) {
+    if (B < 0 || hidden <= 0 || D <= 0)
+        return -1;
+    set_threads(nthreads);
+    #pragma omp parallel for schedule(static)
+    for (int j = 0; j < D; j++) {
+        for (int b = 0; b < B; b++) {
+            double ak = 0.0, av = 0.0;
+            for (int i = 0; i < hidden; i++) {
+                double xi = oracle_bf16_to_f64(x[(size_t)b * hidden + i]);
+                ak += xi * oracle_bf16_to_f64(w_k[(size_t)i * D + j]);
+                av += xi * oracle_bf16_to_f64(w_v[(size_t)i * D + j]);
+            }
+            k_out[(size_t)b * D + j] = ak;
+            v_out[(size_t)b * D + j] = av;
+        }
+    }
+    return 0;
+}
+
+/* Write the new rows: for each sequence b with L_b inside the cache's
+ * capacity (contiguous: L_b < kv_stride; paged: its page-table slot exists
+ * and names a page in [0, num_pages)), row L_b of K and V receives the
+ * encoded values. Other rows are not touched. Returns the rows written. */
+int oracle_kv_append(int B, int D, int kv_dtype, const double* k_new, const double* v_new,
+                     double k_scale, double v_scale, void* k, void* v, const int32_t* seq_lens,
+                     const int32_t* page_table, int pt_stride, int page_size, int64_t kv_stride,
+                     int num_pages) {
+    int written = 0;
+    for (int b = 0; b < B; b++) {
+        int t = seq_lens[b];
+        int64_t row;
+        if (t < 0)
+            continue;
+        if (page_table) {
+            if (t / page_size >= pt_stride)
+                continue;
+            int page = page_table[(size_t)b * pt_stride + t / page_size];
+            if (page < 0 || page >= num_pages)
+                continue;
+            row = (int64_t)page * page_size + t % page_size;
+        } else {
+            if (t >= kv_stride)
+                continue;
+            row = (int64_t)b * kv_stride + t;
+        }
+        for (int d = 0; d < D; d++) {
+            float kf = (float)k_new[(size_t)b * D + d];
+            float vf = (float)v_new[(size_t)b * D + d];
+            if (kv_dtype == OR_FP8_E4M3) {
+                ((uint8_t*)k)[row * D + d] = oracle_f32_to_e4m3(kf / (float)k_scale);
+                ((uint8_t*)v)[row * D + d] = oracle_f32_to_e4m3(vf / (float)v_scale);
+            } else {
+                ((uint16_t*)k)[row * D + d] = oracle_f32_to_bf16(kf);
+                ((uint16_t*)v)[row * D + d] = oracle_f32_to_bf16(vf);
+            }
+        }
+        written++;
+    }
+    return written;
 }

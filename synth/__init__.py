@@ -28,7 +28,7 @@ PAGE_SIZE = 64
 FP8_MAX = 448.0
 
 # fixed order of per-tensor random streams; append only
-_STREAMS = ("q", "k", "v", "seq_lens", "perm", "x", "w_qa", "w_qb", "gamma")
+_STREAMS = ("q", "k", "v", "seq_lens", "perm", "x", "w_qa", "w_qb", "gamma", "w_k", "w_v")
 
 
 def _streams(seed: int) -> dict:
@@ -82,6 +82,7 @@ class Case:
     seq_lens int32 [B]; page_table int32 [B, pt_stride] or None
     k_scale, v_scale  float32 dequant scales (1.0 for bf16)
     x, w_qa, gamma, w_qb  bf16 bits for the Q projection, or None
+    w_k, w_v  bf16 bits [HIDDEN, D] for the new token's K and V, or None
     """
     name: str
     batch: int
@@ -97,6 +98,8 @@ class Case:
     w_qa: Optional[np.ndarray] = None
     gamma: Optional[np.ndarray] = None
     w_qb: Optional[np.ndarray] = None
+    w_k: Optional[np.ndarray] = None
+    w_v: Optional[np.ndarray] = None
     softmax_scale: float = 1.0 / 16.0
     rms_eps: float = 1e-6
     split_tokens: int = 0
@@ -140,7 +143,7 @@ def _kv_tensor(g, shape, kv_dtype):
 def make_case(name: str, batch: int, seq_lens, kv_dtype: str = "bf16", *,
               seed: int = 0, paged: bool = False, with_qproj: bool = False,
               q_std: float = 1.0, split_tokens: int = 0, max_context: int = 0,
-              kv_slack: int = 0) -> Case:
+              kv_slack: int = 0, append_room: int = 0, with_kv_proj: bool = False) -> Case:
     """Build a case. ``seq_lens`` is an int or a sequence of B ints.
 
     Contiguous caches have ``kv_stride = max(L) + kv_slack`` token slots per
@@ -148,6 +151,11 @@ def make_case(name: str, batch: int, seq_lens, kv_dtype: str = "bf16", *,
     caches hold P = sum_b ceil(L_b/64) pages; page_table[b][j] = perm[off_b+j]
     with perm a seeded permutation of [0, P), assigned in (b, j) order. Unused
     page-table entries and cache rows past L_b hold 0 / random data.
+
+    ``append_room`` tokens of room past L_b are reserved for appended rows
+    (contiguous: added to the slack; paged: pages cover L_b + append_room).
+    ``with_kv_proj`` adds the hidden state x and the K and V projection
+    weights, drawn like the Q projection's (std 1/sqrt(HIDDEN)).
     """
     st = _streams(seed)
     L = np.broadcast_to(np.asarray(seq_lens, dtype=np.int32), (batch,)).copy()
@@ -155,9 +163,9 @@ def make_case(name: str, batch: int, seq_lens, kv_dtype: str = "bf16", *,
     case = Case(name=name, batch=batch, kv_dtype=kv_dtype, seq_lens=L,
                 k=None, v=None, seed=seed, split_tokens=split_tokens)
     if paged:
-        npg = (L.astype(np.int64) + PAGE_SIZE - 1) // PAGE_SIZE
+        npg = (L.astype(np.int64) + append_room + PAGE_SIZE - 1) // PAGE_SIZE
         P = int(npg.sum())
-        pt_stride = max(1, (max(maxL, max_context) + PAGE_SIZE - 1) // PAGE_SIZE)
+        pt_stride = max(1, (max(maxL + append_room, max_context) + PAGE_SIZE - 1) // PAGE_SIZE)
         perm = st["perm"].permutation(P).astype(np.int32)
         pt = np.zeros((batch, pt_stride), dtype=np.int32)
         off = 0
@@ -168,7 +176,7 @@ def make_case(name: str, batch: int, seq_lens, kv_dtype: str = "bf16", *,
         case.page_table = pt
         shape = (max(P, 1), PAGE_SIZE, HEAD_DIM)
     else:
-        shape = (batch, maxL + kv_slack, HEAD_DIM)
+        shape = (batch, maxL + kv_slack + append_room, HEAD_DIM)
     case.k, case.k_scale = _kv_tensor(st["k"], shape, kv_dtype)
     case.v, case.v_scale = _kv_tensor(st["v"], shape, kv_dtype)
     if with_qproj:
@@ -179,6 +187,11 @@ def make_case(name: str, batch: int, seq_lens, kv_dtype: str = "bf16", *,
         case.gamma = bf16_bits(np.ones(Q_RANK, dtype=np.float32))
     else:
         case.q = bf16_bits(_normal(st["q"], (batch, NUM_HEADS, HEAD_DIM), q_std))
+    if with_kv_proj:
+        if case.x is None:
+            case.x = bf16_bits(_normal(st["x"], (batch, HIDDEN)))
+        case.w_k = bf16_bits(_normal(st["w_k"], (HIDDEN, HEAD_DIM), 1.0 / math.sqrt(HIDDEN)))
+        case.w_v = bf16_bits(_normal(st["w_v"], (HIDDEN, HEAD_DIM), 1.0 / math.sqrt(HIDDEN)))
     return case
 
 

@@ -352,3 +352,154 @@ def test_config_recipes():
     assert c2.x.shape == (2, 7168) and c2.w_qa.shape == (7168, 2048) and c2.w_qb.shape == (2048, 16384)
     # seeded: same seed, same bytes
     assert np.array_equal(synth.config_case(1).k, c1.k)
+
+
+# ------------------------------------------------------------------ KV append
+
+def _e4m3_finite_positive():
+    t = oracle.e4m3_table()
+    return t[:0x7F]                                      # codes 0x00 .. 0x7e
+
+
+def test_encode_e4m3_matches_torch_in_range():
+    rng = np.random.default_rng(41)
+    for s in (1e-3, 0.1, 1.0, 30.0, 200.0):
+        x = (rng.standard_normal(40000) * s).astype(np.float32)
+        x = x[np.abs(x) < 448]
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(oracle.encode_e4m3(x), ref)
+
+
+def test_encode_e4m3_round_trip_ties_and_saturation():
+    pos = _e4m3_finite_positive()
+    codes = np.arange(0x7F, dtype=np.uint8)
+    # every finite code decodes and encodes back to itself, both signs
+    assert np.array_equal(oracle.encode_e4m3(pos.astype(np.float32)), codes)
+    assert np.array_equal(oracle.encode_e4m3(-pos.astype(np.float32)), codes | 0x80)
+    # midpoints between neighbours (exact in float32) go to the even code,
+    # points just inside either side go to that side
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (pos[:-1] + pos[1:]) / 2)
+    even = np.where(codes[:-1] % 2 == 0, codes[:-1], codes[1:])
+    assert np.array_equal(oracle.encode_e4m3(mid), even)
+    lo = np.nextafter(mid, np.float32(0))
+    hi = np.nextafter(mid, np.float32(np.inf))
+    assert np.array_equal(oracle.encode_e4m3(lo), codes[:-1])
+    assert np.array_equal(oracle.encode_e4m3(hi), codes[1:])
+    # no infinities in the format: everything at or past 448 saturates
+    big = np.array([448, 449, 464, 1e4, 3e38, np.inf], dtype=np.float32)
+    assert np.all(oracle.encode_e4m3(big) == 0x7E)
+    assert np.all(oracle.encode_e4m3(-big) == 0xFE)
+    assert oracle.encode_e4m3(np.array([np.nan], np.float32))[0] & 0x7F == 0x7F
+    # below half the smallest subnormal: zero with the sign
+    assert oracle.encode_e4m3(np.array([2.0 ** -11, -2.0 ** -11], np.float32)).tolist() == [0, 0x80]
+
+
+def test_encode_bf16_matches_torch_and_ties():
+    rng = np.random.default_rng(42)
+    x = (rng.standard_normal(50000) * np.exp(rng.uniform(-20, 20, 50000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.encode_bf16(x), ref)
+    # exact halfway points: bf16 value with low half 0x8000 rounds to even
+    hi = rng.integers(0x0080, 0x7F00, size=4000, dtype=np.uint32)
+    tie = ((hi << 16) | 0x8000).view(np.float32)
+    assert np.array_equal(oracle.encode_bf16(tie), (hi + (hi & 1)).astype(np.uint16))
+    assert oracle.encode_bf16(np.array([np.inf, -np.inf], np.float32)).tolist() == [0x7F80, 0xFF80]
+
+
+def test_encode_monotone():
+    x = np.sort(np.random.default_rng(43).standard_normal(20000).astype(np.float32) * 50)
+    d8 = oracle.decode_e4m3(oracle.encode_e4m3(x))
+    assert np.all(np.diff(d8) >= 0)
+    d16 = oracle.decode_bf16(oracle.encode_bf16(x))
+    assert np.all(np.diff(d16) >= 0)
+
+
+def _tiny_kv_inputs(B, hidden, D, seed):
+    rng = np.random.default_rng(seed)
+    x = synth.bf16_bits(rng.standard_normal((B, hidden)).astype(np.float32))
+    wk = synth.bf16_bits((rng.standard_normal((hidden, D)) / math.sqrt(hidden)).astype(np.float32))
+    wv = synth.bf16_bits((rng.standard_normal((hidden, D)) / math.sqrt(hidden)).astype(np.float32))
+    return x, wk, wv
+
+
+def test_kv_project_matches_numpy_dgemm():
+    x, wk, wv = _tiny_kv_inputs(6, 160, 48, 44)
+    k, v = oracle.kv_project(x, wk, wv)
+    X, WK, WV = (_torch_decode_bf16(a) for a in (x, wk, wv))
+    assert _rel(k, X @ WK) < 1e-13
+    assert _rel(v, X @ WV) < 1e-13
+    # swapping the two weights swaps the outputs
+    k2, v2 = oracle.kv_project(x, wv, wk)
+    assert np.array_equal(k2, v) and np.array_equal(v2, k)
+
+
+def test_kv_project_tiny_decimal():
+    decimal.getcontext().prec = 50
+    Dd = decimal.Decimal
+    x, wk, wv = _tiny_kv_inputs(2, 7, 3, 45)
+    X, WK, WV = (_torch_decode_bf16(a) for a in (x, wk, wv))
+    k, v = oracle.kv_project(x, wk, wv)
+    for b in range(2):
+        for j in range(3):
+            rk = float(sum(Dd(float(X[b, i])) * Dd(float(WK[i, j])) for i in range(7)))
+            rv = float(sum(Dd(float(X[b, i])) * Dd(float(WV[i, j])) for i in range(7)))
+            assert abs(k[b, j] - rk) <= 1e-15 * max(1.0, abs(rk))
+            assert abs(v[b, j] - rv) <= 1e-15 * max(1.0, abs(rv))
+
+
+@pytest.mark.parametrize("kv", [BF16, FP8])
+def test_kv_append_contiguous_writes_one_row(kv):
+    B, S, D = 4, 10, 16
+    raw = np.uint16 if kv == BF16 else np.uint8
+    rng = np.random.default_rng(46)
+    k = rng.integers(0, 0x7E, size=(B, S, D)).astype(raw)
+    v = rng.integers(0, 0x7E, size=(B, S, D)).astype(raw)
+    k0, v0 = k.copy(), v.copy()
+    kn = rng.standard_normal((B, D)) * 3
+    vn = rng.standard_normal((B, D)) * 3
+    L = np.array([0, 5, 9, 10], np.int32)                # the last is past the capacity
+    ks, vs = (0.5, 0.25) if kv == FP8 else (1.0, 1.0)
+    n = oracle.kv_append(kn, vn, k, v, L, kv_dtype=kv, k_scale=ks, v_scale=vs)
+    assert n == 3
+    enc = ((lambda a, s: oracle.encode_bf16(a.astype(np.float32))) if kv == BF16 else
+           (lambda a, s: oracle.encode_e4m3(a.astype(np.float32) / np.float32(s))))
+    for b in range(B):
+        for t in range(S):
+            if b < 3 and t == L[b]:
+                assert np.array_equal(k[b, t], enc(kn[b], ks))
+                assert np.array_equal(v[b, t], enc(vn[b], vs))
+            else:
+                assert np.array_equal(k[b, t], k0[b, t]) and np.array_equal(v[b, t], v0[b, t])
+    # the written row decodes to the value within half a step of the format
+    dec = oracle.decode_bf16 if kv == BF16 else oracle.decode_e4m3
+    got = dec(k[1, 5]) * ks
+    rel = 2.0 ** -8 if kv == BF16 else 2.0 ** -4           # half a unit in the last place
+    assert np.all(np.abs(got - kn[1]) <= rel * np.abs(kn[1]) + (2.0 ** -10) * ks)
+
+
+@pytest.mark.parametrize("kv", [BF16, FP8])
+def test_kv_append_paged_matches_contiguous(kv):
+    """Appending through a page table and gathering the pages back gives the
+    same cache as appending to the contiguous layout."""
+    case = synth.make_case("t", 3, [63, 64, 130], "bf16" if kv == BF16 else "fp8", seed=47,
+                           paged=True, append_room=1)
+    B, D = case.batch, case.k.shape[-1]
+    rng = np.random.default_rng(48)
+    kn, vn = rng.standard_normal((B, D)), rng.standard_normal((B, D))
+    kp, vp = case.k.copy(), case.v.copy()
+    n = oracle.kv_append(kn, vn, kp, vp, case.seq_lens, kv_dtype=kv, k_scale=case.k_scale,
+                         v_scale=case.v_scale, page_table=case.page_table)
+    assert n == B
+    for b in range(B):
+        L1 = case.seq_lens[b] + 1
+        kc, vc = oracle.gather_kv(kp, vp, [L1], 0, page_table=case.page_table[b:b + 1])
+        kc0, vc0 = oracle.gather_kv(case.k, case.v, [L1], 0, page_table=case.page_table[b:b + 1])
+        kk, vv = kc0[None].copy(), vc0[None].copy()
+        oracle.kv_append(kn[b:b + 1], vn[b:b + 1], kk, vv, case.seq_lens[b:b + 1], kv_dtype=kv,
+                         k_scale=case.k_scale, v_scale=case.v_scale)
+        assert np.array_equal(kc, kk[0]) and np.array_equal(vc, vv[0])
+    # pages no sequence owns are untouched
+    owned = np.unique(case.page_table[case.page_table >= 0])
+    free = np.setdiff1d(np.arange(case.k.shape[0]), owned)
+    assert np.array_equal(kp[free], case.k[free]) and np.array_equal(vp[free], case.v[free])
