@@ -23,7 +23,7 @@ MFA_ERR_NOMEM = -3
 MFA_ERR_HIP = -4
 MFA_DTYPE_BF16 = 0
 MFA_DTYPE_FP8_E4M3 = 1
-KERNEL_KINDS = ("attention", "combine", "qproj_down", "rmsnorm", "qproj_up")
+KERNEL_KINDS = ("attention", "combine", "qproj_down", "rmsnorm", "qproj_up", "kv_proj", "kv_write")
 
 
 class MfaError(RuntimeError):
@@ -61,6 +61,8 @@ def _load_lib():
     lib.mfa_qproj.argtypes = [P, P, P, P, P, P, I32, P]
     lib.mfa_qproj.restype = ctypes.c_int
     lib.mfa_decode.argtypes = [P, P, ctypes.POINTER(mfa_kv), P, P, I32, P]
+    lib.mfa_kv_append.argtypes = [P, P, P, P, ctypes.POINTER(mfa_kv), I32, P]
+    lib.mfa_kv_append.restype = ctypes.c_int
     lib.mfa_decode.restype = ctypes.c_int
     lib.mfa_split_tokens.argtypes = [P, I32, I32]
     lib.mfa_split_tokens.restype = I32
@@ -155,6 +157,12 @@ def mfa_qproj(h: int, x, w_qa, rms_w, w_qb, q_out, batch: int, stream=None) -> N
 def mfa_decode(h: int, q, kv: mfa_kv, out, lse_out, batch: int, stream=None) -> None:
     _check(lib.mfa_decode(h, _ptr(q), ctypes.byref(kv), _ptr(out), _ptr(lse_out), batch,
                           _stream(stream)), "mfa_decode")
+
+
+def mfa_kv_append(h: int, x, w_k, w_v, kv: mfa_kv, batch: int, stream=None) -> None:
+    """Writes the new token's K and V rows into kv's cache at row seq_lens[b]."""
+    _check(lib.mfa_kv_append(h, _ptr(x), _ptr(w_k), _ptr(w_v), ctypes.byref(kv), batch,
+                             _stream(stream)), "mfa_kv_append")
 
 
 def mfa_split_tokens(h: int, batch: int, max_seq_len: int = 0) -> int:

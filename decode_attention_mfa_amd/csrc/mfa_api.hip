@@ -57,6 +57,7 @@ struct mfa_ctx {
     int32_t* counters;     // [max_batch], zero between calls
     float* c_part;         // [hidden / kQprojRowsPerSplit][max_batch][q_rank]
     uint16_t* chat;        // [max_batch][q_rank]
+    float* kv_part;        // [2][hidden / kKvRowsPerSplit][max_batch][256]
 };
 
 static bool valid_handle(mfa_handle h) { return h != nullptr && h->magic == kMagic; }
@@ -152,6 +153,7 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     const int64_t bytes_lse = nparts * mfa::kHeads * 4;
     const int64_t bytes_c = (int64_t)(c.hidden / mfa::kQprojRowsPerSplit) * c.max_batch * c.q_rank * 4;
     const int64_t bytes_chat = (int64_t)c.max_batch * c.q_rank * 2;
+    const int64_t bytes_kv = 2 * (int64_t)(c.hidden / mfa::kKvRowsPerSplit) * c.max_batch * mfa::kHeadDim * 4;
     if (max_chunks > (1 << 24) || nparts > (int64_t)1 << 31)
         return fail(MFA_ERR_INVALID, "mfa_create: max_batch * max_context too large");
 
@@ -165,9 +167,10 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
         delete h;
         return hip_fail(e, "mfa_create: device query");
     }
-    void* p[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
-    const int64_t sizes[5] = {bytes_o, bytes_lse, bytes_c, bytes_chat, (int64_t)c.max_batch * 4};
-    for (int i = 0; i < 5; i++) {
+    constexpr int kBuffers = 6;
+    void* p[kBuffers] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    const int64_t sizes[kBuffers] = {bytes_o, bytes_lse, bytes_c, bytes_chat, (int64_t)c.max_batch * 4, bytes_kv};
+    for (int i = 0; i < kBuffers; i++) {
         e = hipMalloc(&p[i], (size_t)sizes[i]);
         if (e != hipSuccess) {
             for (int j = 0; j < i; j++) (void)hipFree(p[j]);
@@ -182,10 +185,11 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     h->c_part = (float*)p[2];
     h->chat = (uint16_t*)p[3];
     h->counters = (int32_t*)p[4];
+    h->kv_part = (float*)p[5];
     e = hipMemset(h->counters, 0, (size_t)c.max_batch * 4);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
-        for (int j = 0; j < 5; j++) (void)hipFree(p[j]);
+        for (int j = 0; j < kBuffers; j++) (void)hipFree(p[j]);
         delete h;
         return hip_fail(e, "mfa_create: clearing the workspace");
     }
@@ -205,6 +209,7 @@ int mfa_destroy(mfa_handle h) {
     (void)hipFree(h->c_part);
     (void)hipFree(h->chat);
     (void)hipFree(h->counters);
+    (void)hipFree(h->kv_part);
     delete h;
     return MFA_OK;
 }
@@ -320,6 +325,42 @@ int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* 
     if (e == hipSuccess && a.n_chunk > a.fuse_max)
         e = timed_launch(h, MFA_KERNEL_COMBINE, st, [&](const mfa::Launch& l) { return mfa::launch_combine(a, batch, l); });
     if (e != hipSuccess) return hip_fail(e, "mfa_decode: launch");
+    return MFA_OK;
+}
+
+int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v, const mfa_kv* kv,
+                  int32_t batch, void* hip_stream) {
+    g_last_error[0] = 0;
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_kv_append: not a live handle");
+    if (!x || !w_k || !w_v) return fail(MFA_ERR_INVALID, "mfa_kv_append: null x, w_k or w_v");
+    int32_t max_len = 0;
+    int rc = check_kv(h, kv, batch, "mfa_kv_append", &max_len);
+    if (rc) return rc;
+    const bool fp8 = h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3;
+    const bool paged = h->cfg.page_size != 0;
+    mfa::KvAppendArgs a;
+    a.x = (const uint16_t*)x;
+    a.w_k = (const uint16_t*)w_k;
+    a.w_v = (const uint16_t*)w_v;
+    a.kv_part = h->kv_part;
+    a.k = (uint8_t*)const_cast<void*>(kv->k);
+    a.v = (uint8_t*)const_cast<void*>(kv->v);
+    a.seq_lens = kv->seq_lens;
+    a.page_table = paged ? kv->page_table : nullptr;
+    a.kv_stride = kv->kv_stride;
+    a.pt_stride = kv->pt_stride;
+    a.num_pages = kv->num_pages;
+    a.batch = batch;
+    a.hidden = h->cfg.hidden;
+    a.ksplit = a.hidden / mfa::kKvRowsPerSplit;
+    a.k_scale = fp8 ? kv->k_scale : 1.0f;
+    a.v_scale = fp8 ? kv->v_scale : 1.0f;
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e = timed_launch(h, MFA_KERNEL_KV_PROJ, st, [&](const mfa::Launch& l) { return mfa::launch_kv_proj(a, l); });
+    if (e == hipSuccess)
+        e = timed_launch(h, MFA_KERNEL_KV_WRITE, st,
+                         [&](const mfa::Launch& l) { return mfa::launch_kv_write(a, fp8, paged, l); });
+    if (e != hipSuccess) return hip_fail(e, "mfa_kv_append: launch");
     return MFA_OK;
 }
 

@@ -72,6 +72,28 @@ struct QprojArgs {
 // a multiple of it.
 constexpr int kQprojRowsPerSplit = 512;
 
+struct KvAppendArgs {
+    const uint16_t* x;      // [B][hidden]
+    const uint16_t* w_k;    // [hidden][256]
+    const uint16_t* w_v;    // [hidden][256]
+    float* kv_part;         // workspace [2][ksplit][B][256] fp32 (K partials, then V)
+    uint8_t* k;             // cache written at row L_b (contiguous or paged)
+    uint8_t* v;
+    const int32_t* seq_lens;
+    const int32_t* page_table;  // nullptr: contiguous
+    int64_t kv_stride;
+    int32_t pt_stride, num_pages;
+    int32_t batch, hidden, ksplit;
+    float k_scale, v_scale;     // FP8: the stored code is E4M3(value / scale); unused for bf16
+};
+
+// The K/V projections split K into blocks of this many rows (hidden is a
+// multiple of 512, so of this too).
+constexpr int kKvRowsPerSplit = 256;
+
+hipError_t launch_kv_proj(const KvAppendArgs& a, const Launch& l);
+hipError_t launch_kv_write(const KvAppendArgs& a, bool fp8, bool paged, const Launch& l);
+
 hipError_t launch_qproj_down(const QprojArgs& a, const Launch& l);
 hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l);
 hipError_t launch_qproj_up(const QprojArgs& a, const Launch& l);

@@ -6,7 +6,11 @@
 //   norm   chat = bf16(sum_split c_part * rsqrt(mean(c^2) + eps) * gamma)
 //   up     q = bf16(chat . W_qb)                   skinny bf16 MFMA GEMM
 //
-// Both GEMMs have few rows (the batch) and read a large row-major [in][out]
+// The same skinny GEMM also computes the new token's key and value rows,
+// x . W_k and x . W_v (hidden -> 256 each, one launch for both weights), for
+// the KV append.
+//
+// The GEMMs have few rows (the batch) and read a large row-major [in][out]
 // weight from HBM exactly once, so they are bandwidth-bound. Each workgroup
 // owns 64 output columns and a range of K; per 64-row K tile, the weight tile
 // (64 x 64) and the matching activation tile (64 rows x 64) stream into an
@@ -60,19 +64,28 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* ptr) {
 
 }  // namespace
 
-// Y[m][n] over m in [64*blockIdx.z, +64) with m < M, n in [64*blockIdx.x, +64),
-// k in [kper*blockIdx.y, +kper) (kper a multiple of 64).
+// Y[m][n] over m in [64*blockIdx.z, +64) with m < M, n in [64*bx, +64),
+// k in [kper*blockIdx.y, +kper) (kper a multiple of 64), where bx =
+// blockIdx.x. A grid of 2 * N/64 columns of blocks computes a second product
+// X . W2 into Y2 with the blocks bx >= N/64 (bx - N/64 there).
 // OUT_BF16: Y is bf16 [M][N]; otherwise fp32 partials [gridDim.y][M][N].
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __restrict__ X, int ldx,
                                                               const uint16_t* __restrict__ W, int N, int kper,
-                                                              int M, void* __restrict__ Y) {
+                                                              int M, void* __restrict__ Y,
+                                                              const uint16_t* __restrict__ W2, void* __restrict__ Y2) {
     // slot: weight tile, then activation tile
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kGemmDepth][2 * kTileBytes];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, lr = l & 15, g = l >> 4;
-    const int n0 = 64 * blockIdx.x;
+    int bx = blockIdx.x;
+    if (bx >= N / 64) {
+        bx -= N / 64;
+        W = W2;
+        Y = Y2;
+    }
+    const int n0 = 64 * bx;
     const int kbeg = kper * blockIdx.y;
     const int m0 = 64 * blockIdx.z;
     const int mt_n = min(4, (M - m0 + 15) / 16);   // 16-row tiles holding real rows
@@ -207,7 +220,8 @@ __global__ __launch_bounds__(256) void mfa_rmsnorm_kernel(const float* __restric
 hipError_t launch_qproj_down(const QprojArgs& a, const Launch& l) {
     const int mblk = (a.batch + 63) / 64;
     return launch_kernel(mfa_skinny_gemm_kernel<false>, dim3(a.rank / 64, a.ksplit, mblk), dim3(256), l, a.x,
-                         a.hidden, a.w_qa, a.rank, a.hidden / a.ksplit, a.batch, (void*)a.c_part);
+                         a.hidden, a.w_qa, a.rank, a.hidden / a.ksplit, a.batch, (void*)a.c_part,
+                         (const uint16_t*)nullptr, (void*)nullptr);
 }
 
 hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l) {
@@ -218,7 +232,17 @@ hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l) {
 hipError_t launch_qproj_up(const QprojArgs& a, const Launch& l) {
     const int mblk = (a.batch + 63) / 64;
     return launch_kernel(mfa_skinny_gemm_kernel<true>, dim3(a.nq / 64, 1, mblk), dim3(256), l,
-                         (const uint16_t*)a.chat, a.rank, a.w_qb, a.nq, a.rank, a.batch, (void*)a.q_out);
+                         (const uint16_t*)a.chat, a.rank, a.w_qb, a.nq, a.rank, a.batch, (void*)a.q_out,
+                         (const uint16_t*)nullptr, (void*)nullptr);
+}
+
+hipError_t launch_kv_proj(const KvAppendArgs& a, const Launch& l) {
+    const int mblk = (a.batch + 63) / 64;
+    float* kp = a.kv_part;
+    float* vp = a.kv_part + (int64_t)a.ksplit * a.batch * kHeadDim;
+    return launch_kernel(mfa_skinny_gemm_kernel<false>, dim3(2 * kHeadDim / 64, a.ksplit, mblk), dim3(256), l,
+                         a.x, a.hidden, a.w_k, kHeadDim, a.hidden / a.ksplit, a.batch, (void*)kp, a.w_v,
+                         (void*)vp);
 }
 
 }  // namespace mfa

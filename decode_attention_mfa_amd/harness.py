@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from . import (MFA_DTYPE_BF16, MFA_DTYPE_FP8_E4M3, make_config, make_kv, mfa_create,
-               mfa_decode, mfa_destroy, mfa_qproj)
+               mfa_decode, mfa_destroy, mfa_kv_append, mfa_qproj)
 
 HEADS, HEAD_DIM = 64, 256
 
@@ -42,6 +42,8 @@ class DeviceCase:
     w_qa: Optional[torch.Tensor] = None
     gamma: Optional[torch.Tensor] = None
     w_qb: Optional[torch.Tensor] = None
+    w_k: Optional[torch.Tensor] = None
+    w_v: Optional[torch.Tensor] = None
     softmax_scale: float = 1.0 / 16.0
     rms_eps: float = 1e-6
     split_tokens: int = 0
@@ -64,6 +66,7 @@ def to_device(case, device="cuda") -> DeviceCase:
         q=_dev(case.q, device), page_table=_dev(case.page_table, device), k_scale=case.k_scale,
         v_scale=case.v_scale, x=_dev(case.x, device), w_qa=_dev(case.w_qa, device),
         gamma=_dev(case.gamma, device), w_qb=_dev(case.w_qb, device),
+        w_k=_dev(getattr(case, "w_k", None), device), w_v=_dev(getattr(case, "w_v", None), device),
         softmax_scale=case.softmax_scale, rms_eps=case.rms_eps, split_tokens=case.split_tokens)
 
 
@@ -88,6 +91,11 @@ def qproj(h: int, dc: DeviceCase, q_out: Optional[torch.Tensor] = None, stream=N
         q_out = torch.empty((dc.batch, HEADS, HEAD_DIM), dtype=torch.int16, device=dc.x.device)
     mfa_qproj(h, dc.x, dc.w_qa, dc.gamma, dc.w_qb, q_out, dc.batch, stream)
     return q_out
+
+
+def kv_append(h: int, dc: DeviceCase, stream=None, max_seq_len: int = 0) -> None:
+    """Write the new token's K and V rows at row seq_lens[b] of dc's cache."""
+    mfa_kv_append(h, dc.x, dc.w_k, dc.w_v, dc.kv(max_seq_len), dc.batch, stream)
 
 
 def decode(h: int, dc: DeviceCase, q: Optional[torch.Tensor] = None, out=None, lse=None,

@@ -78,7 +78,7 @@ typedef struct {
  *     page_table[b * pt_stride + t / 64].
  * Element type: bf16 or E4M3 per the handle's kv_dtype. An FP8 element's
  * value is decode(code) * k_scale (keys) or * v_scale (values). Only rows
- * t < seq_lens[b] are read. */
+ * t < seq_lens[b] are read; mfa_kv_append writes row seq_lens[b]. */
 typedef struct {
     const void* k;
     const void* v;
@@ -87,7 +87,8 @@ typedef struct {
     const int32_t* seq_lens;    /* [batch], 0 <= L_b <= max_seq_len (values outside are clamped) */
     const int32_t* page_table;  /* [batch][pt_stride] int32, or NULL when contiguous */
     int32_t pt_stride;          /* paged: entries per page-table row, >= ceil(max_seq_len/64) */
-    int32_t num_pages;          /* paged: pool size in pages (documentation; not checked on device) */
+    int32_t num_pages;          /* paged: pool size in pages, >= 1 (mfa_kv_append skips rows on
+                                   pages outside it; mfa_decode does not check on device) */
     int64_t kv_stride;          /* contiguous: token slots per sequence, >= max_seq_len */
     int32_t max_seq_len;        /* (host) upper bound of seq_lens in this call, sizes the
                                    launch; 0 = the handle's max_context */
@@ -98,8 +99,9 @@ typedef struct {
  *   max_batch * ceil(max_context / C) * 64 * (256 + 1) * 4 bytes of chunk
  *   partials, C = split_tokens or, when that is 0, 256 (the smallest chunk
  *   chosen per call), max_batch 4-byte arrival counters (zeroed here, left
- *   at zero by every call), plus Q-projection scratch of
- *   max_batch * q_rank * (4 * hidden / 512 + 2) bytes.
+ *   at zero by every call), Q-projection scratch of
+ *   max_batch * q_rank * (4 * hidden / 512 + 2) bytes, and K/V-projection
+ *   partials of 2 * (hidden / 256) * max_batch * 256 * 4 bytes.
  * On success stores the handle in *out (host pointer) and returns MFA_OK. */
 int mfa_create(const mfa_config* cfg, mfa_handle* out);
 
@@ -134,6 +136,25 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
 int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out,
                int32_t batch, void* hip_stream);
 
+/* KV append: the new token's key and value rows, written into the cache
+ * before that token's attention (Step-3 Key points: one shared key head and
+ * one shared value head of 256, so one K row and one V row per token; the
+ * FP8 cache of the same Key points; pages as in PagedAttention):
+ *   k_new = x . w_k,  v_new = x . w_v      x [batch][hidden] bf16,
+ *                                          w_k, w_v [hidden][256] bf16
+ * accumulated in fp32, then stored at row L_b = kv->seq_lens[b] of sequence b
+ * (the layout rules of mfa_kv) as bf16 by round-to-nearest-even, or for an
+ * FP8 handle as the E4M3 code of k_new / k_scale (v_new / v_scale), rounded to
+ * nearest even, saturating at +-448. The library WRITES through kv->k and
+ * kv->v here (they must be writable device memory); nothing else in the cache
+ * changes and seq_lens is not advanced (the caller attends with L_b + 1).
+ * A sequence whose row does not exist is skipped, not an error: L_b < 0;
+ * contiguous, L_b >= kv_stride; paged, L_b / 64 >= pt_stride or a page
+ * number outside [0, num_pages) (the caller allocates pages). The other
+ * kv fields are checked as for mfa_decode. 1 <= batch <= max_batch. */
+int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v,
+                  const mfa_kv* kv, int32_t batch, void* hip_stream);
+
 /* The split-K chunk (tokens) mfa_decode uses for this batch and kv->max_seq_len. */
 int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len);
 
@@ -150,11 +171,13 @@ enum mfa_kernel_kind {
     MFA_KERNEL_QPROJ_DOWN = 2,  /* x . w_qa */
     MFA_KERNEL_RMSNORM = 3,     /* bottleneck RMSNorm */
     MFA_KERNEL_QPROJ_UP = 4,    /* chat . w_qb */
-    MFA_KERNEL_KINDS = 5
+    MFA_KERNEL_KV_PROJ = 5,     /* x . w_k and x . w_v (K-split partials) */
+    MFA_KERNEL_KV_WRITE = 6,    /* partial sums, encoding and the row write */
+    MFA_KERNEL_KINDS = 7
 };
 
 /* Per-kernel timing for benchmarks, off by default. While enabled, every
- * kernel that mfa_decode or mfa_qproj launches is bracketed by a pair of
+ * kernel that mfa_decode, mfa_qproj or mfa_kv_append launches is bracketed by a pair of
  * hipEvents recorded on the call's stream (events are created here, on the
  * current device). enable = 0 releases them. */
 int mfa_profile_enable(mfa_handle h, int enable);

@@ -18,7 +18,7 @@ def _header_functions():
 def test_header_declares_the_boundary():
     names = _header_functions()
     for n in ("mfa_create", "mfa_qproj", "mfa_decode", "mfa_destroy", "mfa_status_string",
-              "mfa_last_error", "mfa_debug_gather_kv", "mfa_split_tokens"):
+              "mfa_last_error", "mfa_debug_gather_kv", "mfa_split_tokens", "mfa_kv_append"):
         assert n in names
 
 
@@ -66,6 +66,8 @@ def test_null_arguments_are_rejected():
     assert "handle" in m.mfa_last_error()
     assert m.lib.mfa_qproj(None, None, None, None, None, None, 1, None) == m.MFA_ERR_INVALID
     assert m.lib.mfa_debug_gather_kv(None, ctypes.byref(kv), 0, None, None, None) == m.MFA_ERR_INVALID
+    assert m.lib.mfa_kv_append(None, None, None, None, ctypes.byref(kv), 1, None) == m.MFA_ERR_INVALID
+    assert "handle" in m.mfa_last_error()
     assert m.lib.mfa_destroy(None) == m.MFA_OK
     with pytest.raises(m.MfaError):
         m.mfa_decode(None, 0, kv, 0, 0, 1, stream=0)
