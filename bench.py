@@ -5,7 +5,11 @@
 
 A step is one pass of the hot path over one batch: the decode attention
 (chunked scores, online softmax, P.V, log-sum-exp merge) and, for the
-full-layer workload, the Q projection with RMSNorm before it. Inputs are
+full-layer workload, the Q projection with RMSNorm before it. The two
+"+append" workloads add the KV append of the new token before the attention
+(its K and V projections, encoded and written at row L_b), which then reads
+L_b + 1 rows: the full layer as a complete decode step, and the ragged paged
+FP8 batch writing into its pool. Inputs are
 seeded synthetic tensors already resident in HBM; several copies are rotated
 so that consecutive steps do not find their KV cache in the 256 MB MALL.
 
@@ -34,13 +38,19 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MFA decode tokens/s per layer (1 GPU) + achieved HBM GB/s vs roofline"
 HBM_PEAK_GBPS = 8000.0
-WORKLOADS = {"tiny": 1, "full_layer": 2, "fp8_contig": 3, "paged_ragged": 4, "long_splitk": 5}
+WORKLOADS = {"tiny": 1, "full_layer": 2, "fp8_contig": 3, "paged_ragged": 4, "long_splitk": 5,
+             "decode_step": 2, "paged_append": 4}
+APPEND = ("decode_step", "paged_append")
 DESCRIPTION = {
     "tiny": "B=1, L=256, bf16 KV, contiguous, decode only",
     "full_layer": "B=32, L=4096, bf16 KV, contiguous, Q projection 7168->2048 (RMSNorm)->64x256 + decode",
     "fp8_contig": "B=128, L=4096, FP8-E4M3 KV (per-tensor scales), contiguous, decode only",
     "paged_ragged": "B=384, L~U[1024,8192], FP8-E4M3 KV, 64-token pages, permuted page table, decode only",
     "long_splitk": "B=8, L=32768 x4 + 65536 x4, bf16 KV, split-K 512-token chunks, decode only",
+    "decode_step": "B=32, L=4096, bf16 KV, contiguous: Q projection + KV append (7168->256 x2, row L_b) "
+                   "+ decode over L_b+1",
+    "paged_append": "B=384, L~U[1024,8192], FP8-E4M3 KV, 64-token pages: KV append (7168->256 x2, E4M3, "
+                    "row L_b) + decode over L_b+1",
 }
 # sources that decide the attention kernel's memory traffic (kernel, launch
 # shape, split and merge policy); the stored HBM counters hold for this hash
@@ -62,29 +72,45 @@ def attn_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(case, attention_writes_out: bool):
+def algorithmic_bytes(case, attention_writes_out: bool, append: bool = False):
     """(attention-kernel bytes, whole-step bytes) the method must move.
     Attention: every cached K and V row t < L_b (512 B per token with FP8,
-    1024 B with bf16), Q (32 KB per sequence), the lengths and (paged) the
-    page-table entries it reads, and the bf16 output (32 KB per sequence)
-    when the attention kernel writes it (no separate merge launch). Step:
-    all of that plus the output, and for the full layer x, gamma and both
-    projection weights (Q is then produced on the device, not read)."""
+    1024 B with bf16; t <= L_b after an append), Q (32 KB per sequence), the
+    lengths and (paged) the page-table entries it reads, and the bf16 output
+    (32 KB per sequence) when the attention kernel writes it (no separate
+    merge launch). Step: all of that plus the output; with the Q projection,
+    x, gamma and both projection weights (Q is then produced on the device,
+    not read); with the append, x, W_k, W_v, the lengths and page-table
+    entries it reads and the K and V rows it writes."""
     import numpy as np
     B = case.batch
-    kv = case.kv_bytes_read()
+    L = case.seq_lens.astype(np.int64) + (1 if append else 0)
+    elem = 1 if case.kv_dtype == "fp8" else 2
+    kv = int(L.sum()) * 2 * 256 * elem
     q = B * 64 * 256 * 2
     o = B * 64 * 256 * 2
     meta = B * 4
     if case.paged:
-        meta += int(((case.seq_lens.astype(np.int64) + 63) // 64).sum()) * 4
+        meta += int(((L + 63) // 64).sum()) * 4
     attn = kv + q + meta + (o if attention_writes_out else 0)
     step = kv + q + meta + o
-    if case.x is not None:
+    if case.w_qa is not None:
         step += case.x.nbytes + case.w_qa.nbytes + case.w_qb.nbytes + case.gamma.nbytes
         attn -= q
         step -= q
+    if append:
+        step += case.w_k.nbytes + case.w_v.nbytes + B * 4 + B * 2 * 256 * elem
+        step += case.x.nbytes if case.w_qa is None else 0
+        step += B * 4 if case.paged else 0
     return attn, step
+
+
+def append_bytes(case):
+    """Bytes the KV append must move: x, W_k, W_v, the lengths (and page-table
+    entries) it reads and the two rows per sequence it writes."""
+    elem = 1 if case.kv_dtype == "fp8" else 2
+    return (case.x.nbytes + case.w_k.nbytes + case.w_v.nbytes + case.batch * (8 if case.paged else 4)
+            + case.batch * 2 * 256 * elem)
 
 
 def sample_case(case, n):
@@ -109,15 +135,22 @@ def cpu_baseline(case, budget_s: float):
     """The fp64 oracle, as it stands, on the first n sequences; n chosen from
     a one-sequence probe so that the run takes about budget_s seconds."""
     import oracle
+
+    def work(s):
+        if s.w_k is not None:
+            oracle.kv_project(s.x, s.w_k, s.w_v)
+        oracle.case_attention(s)
+
     t0 = time.perf_counter()
-    oracle.case_attention(sample_case(case, 1))
+    work(sample_case(case, 1))
     t1 = time.perf_counter() - t0
     n = max(1, min(case.batch, int(budget_s / max(t1, 1e-3))))
     s = sample_case(case, n)
     t0 = time.perf_counter()
-    oracle.case_attention(s)
+    work(s)
     dt = time.perf_counter() - t0
-    what = "attention" if case.x is None else "Q projection + attention"
+    what = " + ".join(w for w, on in (("Q projection", case.w_qa is not None),
+                                       ("K/V projection", case.w_k is not None), ("attention", True)) if on)
     return {"value": n / dt, "unit": "tokens/s/layer", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"{what} of the first {n} of {case.batch} sequences, fp64, {dt:.1f} s"}
 
@@ -173,9 +206,10 @@ def main():
     wl = args.workload
     log(f"[bench] generating workload {wl}: {DESCRIPTION[wl]}")
     t0 = time.perf_counter()
-    case = synth.config_case(WORKLOADS[wl])
+    append = wl in APPEND
+    case = synth.config_case(WORKLOADS[wl], append=append)
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s")
-    _, step_bytes = algorithmic_bytes(case, True)
+    _, step_bytes = algorithmic_bytes(case, True, append)
 
     dc = harness.to_device(case)
     # rotate copies of the per-step inputs so that no step finds them in the MALL
@@ -189,17 +223,26 @@ def main():
         if dc.q is not None:
             c.q = dc.q.clone()
         if dc.x is not None:
-            c.x, c.w_qa, c.w_qb = dc.x.clone(), dc.w_qa.clone(), dc.w_qb.clone()
+            c.x = dc.x.clone()
+        if dc.w_qa is not None:
+            c.w_qa, c.w_qb = dc.w_qa.clone(), dc.w_qb.clone()
+        if dc.w_k is not None:
+            c.w_k, c.w_v = dc.w_k.clone(), dc.w_v.clone()
         sets.append(c)
     cold = nrot * step_bytes > 512e6
 
-    h = harness.create_handle(dc, split_tokens=args.split)
-    split = mfa.mfa_split_tokens(h, dc.batch, dc.max_len)
+    # after the append the attention reads L_b + 1 rows
+    attn_lens = dc.seq_lens + 1 if append else dc.seq_lens
+    attn_max = dc.max_len + 1 if append else dc.max_len
+    h = harness.create_handle(dc, split_tokens=args.split, max_context=attn_max)
+    split = mfa.mfa_split_tokens(h, dc.batch, attn_max)
     stream = torch.cuda.Stream()
     outs = [harness.alloc_outputs(dc) for _ in range(nrot)]
     qbufs = [torch.empty((dc.batch, 64, 256), dtype=torch.int16, device="cuda") for _ in range(nrot)]
 
     kvs = [c.kv() for c in sets]
+    attn_kvs = [mfa.make_kv(c.k, c.v, attn_lens, page_table=c.page_table, k_scale=c.k_scale,
+                            v_scale=c.v_scale, max_seq_len=attn_max) for c in sets]
 
     def step(i):
         s = sets[i % nrot]
@@ -208,7 +251,10 @@ def main():
         if s.q is None:
             q = qbufs[i % nrot]
             mfa.mfa_qproj(h, s.x, s.w_qa, s.gamma, s.w_qb, q, s.batch, stream)
-        mfa.mfa_decode(h, q, kvs[i % nrot], o, l, s.batch, stream)
+        if append:
+            # writes row L_b (the same row every step: the cache stays as it is)
+            mfa.mfa_kv_append(h, s.x, s.w_k, s.w_v, kvs[i % nrot], s.batch, stream)
+        mfa.mfa_decode(h, q, attn_kvs[i % nrot], o, l, s.batch, stream)
 
     def run(n):
         torch.cuda.synchronize()
@@ -240,7 +286,7 @@ def main():
 
     ms_per_step = dt * 1e3 / args.steps
     value = dc.batch / (ms_per_step / 1e3)
-    attn_bytes, _ = algorithmic_bytes(case, prof["combine"][0] == 0)
+    attn_bytes, _ = algorithmic_bytes(case, prof["combine"][0] == 0, append)
     n_attn, ms_attn = prof["attention"]
     attn_ms = ms_attn / max(n_attn, 1)
     achieved = attn_bytes / (attn_ms / 1e3) / 1e9
@@ -268,6 +314,14 @@ def main():
                                "pass of the timed steps"},
         "kernels": kernels,
     }
+    if append:
+        n_p, ms_p = prof["kv_proj"]
+        n_w, ms_w = prof["kv_write"]
+        ab = append_bytes(case)
+        app_us = (ms_p / max(n_p, 1) + ms_w / max(n_w, 1)) * 1e3
+        result["kv_append"] = {"algorithmic_bytes": ab, "kernels_us": round(app_us, 2),
+                               "achieved_gbps": round(ab / (app_us / 1e6) / 1e9, 1),
+                               "frac": round(ab / (app_us / 1e6) / 1e9 / HBM_PEAK_GBPS, 4)}
     if args.cpu_seconds > 0:
         log("[bench] timing the fp64 CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

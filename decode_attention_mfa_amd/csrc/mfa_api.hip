@@ -88,6 +88,18 @@ static void profiler_release(Profiler& p) {
 
 static int round_up(int64_t a, int64_t m) { return (int)(((a + m - 1) / m) * m); }
 
+// K splits of the K/V projections: the most (256 rows each, the fewest
+// tiles per workgroup) that keep the launch within about two workgroups per
+// compute unit (8 column blocks of 64 for K and V, one row block per 64
+// sequences); halved (rows per split doubled) while it would exceed that and
+// the rows still divide hidden.
+static int32_t kv_ksplit(int32_t hidden, int32_t batch) {
+    const int64_t col_row_blocks = 2 * (mfa::kHeadDim / 64) * (int64_t)((batch + 63) / 64);
+    int32_t rows = mfa::kKvRowsPerSplit;
+    while (col_row_blocks * (hidden / rows) > 512 && hidden % (2 * rows) == 0) rows *= 2;
+    return hidden / rows;
+}
+
 static int32_t choose_split(const mfa_ctx* h, int32_t batch, int32_t max_len) {
     if (h->cfg.split_tokens > 0) return h->cfg.split_tokens;
     if (max_len <= 0) return kMinAutoSplit;
@@ -352,7 +364,7 @@ int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v,
     a.num_pages = kv->num_pages;
     a.batch = batch;
     a.hidden = h->cfg.hidden;
-    a.ksplit = a.hidden / mfa::kKvRowsPerSplit;
+    a.ksplit = kv_ksplit(a.hidden, batch);
     a.k_scale = fp8 ? kv->k_scale : 1.0f;
     a.v_scale = fp8 ? kv->v_scale : 1.0f;
     hipStream_t st = (hipStream_t)hip_stream;

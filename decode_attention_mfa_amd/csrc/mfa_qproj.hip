@@ -14,7 +14,9 @@
 // weight from HBM exactly once, so they are bandwidth-bound. Each workgroup
 // owns 64 output columns and a range of K; per 64-row K tile, the weight tile
 // (64 x 64) and the matching activation tile (64 rows x 64) stream into an
-// LDS ring by direct DMA, eight tiles deep. The weight tile comes back
+// LDS ring by direct DMA, three tiles deep (48 KB of LDS, so that several
+// workgroups share a compute unit: occupancy hides more of the load latency
+// than a deeper ring in one workgroup does). The weight tile comes back
 // transposed with ds_read_b64_tr_b16 as MFMA B operands (the contraction
 // index is the weight's row), the activation tile as A operands.
 #include "mfa_device.h"
@@ -24,7 +26,7 @@ namespace mfa {
 
 namespace {
 
-constexpr int kGemmDepth = 8;             // K tiles in the ring
+constexpr int kGemmDepth = 3;             // K tiles in the ring
 constexpr int kTileBytes = 64 * 128;      // 64 rows x 64 bf16
 
 // 16-byte chunk positions within a 128-byte tile row. Weight rows: swizzled
@@ -39,11 +41,16 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 }
 
 // 16 bytes per lane from global memory into LDS (lane i lands at
-// lds_dst + 16*i; lds_dst wave-uniform, through M0), streaming (nt). Inline
-// asm so that the compiler does not order later LDS accesses behind it; the
-// ring's own waits order the reads.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+// lds_dst + 16*i; lds_dst wave-uniform, through M0). Inline asm so that the
+// compiler does not order later LDS accesses behind it; the ring's own waits
+// order the reads. Weight tiles are read once: streaming hint (nt). The
+// activation tiles are re-read by every column block: default cache policy,
+// so they stay in L2.
+__device__ __forceinline__ void dma16_stream(const void* sbase, uint32_t voff, uint32_t lds_dst) {
     asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds_dst) : "memory");
+}
+__device__ __forceinline__ void dma16_keep(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_dst) : "memory");
 }
 
 template <int N>
@@ -64,18 +71,25 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* ptr) {
 
 }  // namespace
 
-// Y[m][n] over m in [64*blockIdx.z, +64) with m < M, n in [64*bx, +64),
+// Y[m][n] over m in [MR*blockIdx.z, +MR) with m < M, n in [64*bx, +64),
 // k in [kper*blockIdx.y, +kper) (kper a multiple of 64), where bx =
 // blockIdx.x. A grid of 2 * N/64 columns of blocks computes a second product
 // X . W2 into Y2 with the blocks bx >= N/64 (bx - N/64 there).
+// MR (32 or 64) rows per block: 32 when the batch fits, so that the
+// activation tile carries no repeated rows.
 // OUT_BF16: Y is bf16 [M][N]; otherwise fp32 partials [gridDim.y][M][N].
-template <bool OUT_BF16>
+template <bool OUT_BF16, int MR>
 __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __restrict__ X, int ldx,
                                                               const uint16_t* __restrict__ W, int N, int kper,
                                                               int M, void* __restrict__ Y,
                                                               const uint16_t* __restrict__ W2, void* __restrict__ Y2) {
-    // slot: weight tile, then activation tile
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kGemmDepth][2 * kTileBytes];
+    static_assert(MR == 32 || MR == 64, "rows per block");
+    constexpr int MT = MR / 16;            // 16-row MFMA tiles
+    constexpr int XI = MR / 32;            // activation DMA instructions per wave and tile
+    constexpr int OPS = 2 + XI;            // DMA instructions per wave and tile
+    constexpr int kSlot = kTileBytes + MR * 128;
+    // slot: weight tile (64 rows x 128 B), then activation tile (MR rows x 128 B)
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kGemmDepth][kSlot];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, lr = l & 15, g = l >> 4;
@@ -87,37 +101,43 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
     }
     const int n0 = 64 * bx;
     const int kbeg = kper * blockIdx.y;
-    const int m0 = 64 * blockIdx.z;
-    const int mt_n = min(4, (M - m0 + 15) / 16);   // 16-row tiles holding real rows
+    const int m0 = MR * blockIdx.z;
+    const int mt_n = min(MT, (M - m0 + 15) / 16);   // 16-row tiles holding real rows
     const int ntiles = kper / 64;
 
-    // DMA lane offsets (loop-invariant). Instruction i of wave w fills tile
-    // rows 16w + 8i + l/8; lane l lands at chunk position l % 8 of its row
-    // and fetches the data chunk the swizzle puts there. Activation rows past
-    // M repeat row M-1 (in bounds; their products are never stored).
-    uint32_t woff[2], xoff[2];
+    // DMA lane offsets (loop-invariant). Weight instruction i of wave w fills
+    // tile rows 16w + 8i + l/8, activation instruction i rows MR/4*w + 8i +
+    // l/8; lane l lands at chunk position l % 8 of its row and fetches the
+    // data chunk the swizzle puts there. Activation rows past M repeat row
+    // M-1 (in bounds; their products are never stored).
+    uint32_t woff[2], xoff[XI];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int r = 16 * w + 8 * i + (l >> 3);
         woff[i] = (uint32_t)(r * N * 2 + 16 * ((l & 7) ^ wswz(r)));
-        const int xr = min(m0 + r, M - 1) - m0;   // row within this 64-row block
+    }
+#pragma unroll
+    for (int i = 0; i < XI; i++) {
+        const int r = MR / 4 * w + 8 * i + (l >> 3);
+        const int xr = min(m0 + r, M - 1) - m0;   // row within this block
         xoff[i] = (uint32_t)(xr * ldx * 2 + 16 * ((l & 7) ^ xswz(r)));
     }
     auto issue = [&](int tile) {   // clamped to the last tile
         const int k0 = kbeg + 64 * min(tile, ntiles - 1);
         const uint8_t* wb = uniform_ptr(W + (int64_t)k0 * N + n0);
         const uint8_t* xb = uniform_ptr(X + (int64_t)m0 * ldx + k0);
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr_of(ring[tile % kGemmDepth]) + 2048 * w);
+        const uint32_t slot = lds_addr_of(ring[tile % kGemmDepth]);
+        const uint32_t wdst = __builtin_amdgcn_readfirstlane(slot + 2048 * w);
+        const uint32_t xdst = __builtin_amdgcn_readfirstlane(slot + kTileBytes + MR * 32 * w);
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            dma16(wb, woff[i], dst + 1024 * i);
-            dma16(xb, xoff[i], dst + kTileBytes + 1024 * i);
-        }
+        for (int i = 0; i < 2; i++) dma16_stream(wb, woff[i], wdst + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < XI; i++) dma16_keep(xb, xoff[i], xdst + 1024 * i);
     };
 
-    f32x4 acc[4];
+    f32x4 acc[MT];
 #pragma unroll
-    for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; mt++) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
     for (int s = 0; s < kGemmDepth - 1; s++) issue(s);
@@ -125,7 +145,7 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
         // this wave's rows of the tile have landed once at most the younger
         // tiles' loads are in flight; the barrier shows every wave's rows and
         // frees the slot of the previous tile
-        wait_vmem<(kGemmDepth - 2) * 4>();
+        wait_vmem<(kGemmDepth - 2) * OPS>();
         lds_barrier();
         issue(tile + kGemmDepth - 1);
         const uint8_t* wt = ring[tile % kGemmDepth];
@@ -143,7 +163,7 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
             const u32x2 u0 = bitcast<u32x2>(b0), u1 = bitcast<u32x2>(b1);
             const bf16x8 bop = bitcast<bf16x8>(u32x4{u0.x, u0.y, u1.x, u1.y});
 #pragma unroll
-            for (int mt = 0; mt < 4; mt++) {
+            for (int mt = 0; mt < MT; mt++) {
                 if (mt < mt_n) {
                     // A operand: X[m0 + 16mt + lr][k = 32ks + 8g + j]
                     const int r = 16 * mt + lr;
@@ -157,7 +177,7 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
 
     const int n = n0 + 16 * w + lr;
 #pragma unroll
-    for (int mt = 0; mt < 4; mt++) {
+    for (int mt = 0; mt < MT; mt++) {
         if (mt >= mt_n) continue;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -217,11 +237,20 @@ __global__ __launch_bounds__(256) void mfa_rmsnorm_kernel(const float* __restric
     }
 }
 
+// Rows per block: 32 when the whole batch fits in one such block, else 64.
+template <bool OUT_BF16>
+static hipError_t launch_skinny(int gx, int gy, const uint16_t* X, int ldx, const uint16_t* W, int N, int kper,
+                                int M, void* Y, const uint16_t* W2, void* Y2, const Launch& l) {
+    if (M <= 32)
+        return launch_kernel(mfa_skinny_gemm_kernel<OUT_BF16, 32>, dim3(gx, gy, 1), dim3(256), l, X, ldx, W, N,
+                             kper, M, Y, W2, Y2);
+    return launch_kernel(mfa_skinny_gemm_kernel<OUT_BF16, 64>, dim3(gx, gy, (M + 63) / 64), dim3(256), l, X, ldx,
+                         W, N, kper, M, Y, W2, Y2);
+}
+
 hipError_t launch_qproj_down(const QprojArgs& a, const Launch& l) {
-    const int mblk = (a.batch + 63) / 64;
-    return launch_kernel(mfa_skinny_gemm_kernel<false>, dim3(a.rank / 64, a.ksplit, mblk), dim3(256), l, a.x,
-                         a.hidden, a.w_qa, a.rank, a.hidden / a.ksplit, a.batch, (void*)a.c_part,
-                         (const uint16_t*)nullptr, (void*)nullptr);
+    return launch_skinny<false>(a.rank / 64, a.ksplit, a.x, a.hidden, a.w_qa, a.rank, a.hidden / a.ksplit, a.batch,
+                                (void*)a.c_part, nullptr, nullptr, l);
 }
 
 hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l) {
@@ -230,19 +259,15 @@ hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l) {
 }
 
 hipError_t launch_qproj_up(const QprojArgs& a, const Launch& l) {
-    const int mblk = (a.batch + 63) / 64;
-    return launch_kernel(mfa_skinny_gemm_kernel<true>, dim3(a.nq / 64, 1, mblk), dim3(256), l,
-                         (const uint16_t*)a.chat, a.rank, a.w_qb, a.nq, a.rank, a.batch, (void*)a.q_out,
-                         (const uint16_t*)nullptr, (void*)nullptr);
+    return launch_skinny<true>(a.nq / 64, 1, a.chat, a.rank, a.w_qb, a.nq, a.rank, a.batch, (void*)a.q_out, nullptr,
+                               nullptr, l);
 }
 
 hipError_t launch_kv_proj(const KvAppendArgs& a, const Launch& l) {
-    const int mblk = (a.batch + 63) / 64;
     float* kp = a.kv_part;
     float* vp = a.kv_part + (int64_t)a.ksplit * a.batch * kHeadDim;
-    return launch_kernel(mfa_skinny_gemm_kernel<false>, dim3(2 * kHeadDim / 64, a.ksplit, mblk), dim3(256), l,
-                         a.x, a.hidden, a.w_k, kHeadDim, a.hidden / a.ksplit, a.batch, (void*)kp, a.w_v,
-                         (void*)vp);
+    return launch_skinny<false>(2 * kHeadDim / 64, a.ksplit, a.x, a.hidden, a.w_k, kHeadDim, a.hidden / a.ksplit,
+                                a.batch, (void*)kp, a.w_v, (void*)vp, l);
 }
 
 }  // namespace mfa

@@ -199,9 +199,14 @@ def make_case(name: str, batch: int, seq_lens, kv_dtype: str = "bf16", *,
 # contiguous, (4) FP8 paged ragged, (5) long-context split-K. Seeds 1000+i.
 
 def config_case(i: int, *, batch: Optional[int] = None, scale_len: float = 1.0,
-                q_std: float = 1.0) -> Case:
+                q_std: float = 1.0, append: bool = False) -> Case:
     """Workload ``i`` (1..5). ``batch`` and ``scale_len`` shrink it for tests
-    (same recipe, smaller sizes); the defaults give the full size."""
+    (same recipe, smaller sizes); the defaults give the full size.
+    ``append`` adds the new token's K/V projection weights (and x) and one
+    row of cache room per sequence, for the KV-append step; the other tensors
+    are unchanged except a paged pool's page count and permutation."""
+    if append:
+        return _with_append(config_case(i, batch=batch, scale_len=scale_len, q_std=q_std))
     seed = 1000 + i
     if i == 1:
         B = batch or 1
@@ -228,3 +233,13 @@ def config_case(i: int, *, batch: Optional[int] = None, scale_len: float = 1.0,
                      dtype=np.int32)
         return make_case("long_splitk", B, L, "bf16", seed=seed, q_std=q_std, split_tokens=512)
     raise ValueError(f"no workload {i}")
+
+
+def _with_append(base: Case) -> Case:
+    c = make_case(base.name + "_append", base.batch, base.seq_lens, base.kv_dtype, seed=base.seed,
+                  paged=base.paged, with_qproj=base.q is None, q_std=1.0, split_tokens=base.split_tokens,
+                  max_context=int(base.seq_lens.max()) + 1 if base.paged else 0, append_room=1,
+                  with_kv_proj=True)
+    if base.q is not None:
+        c.q = base.q
+    return c
