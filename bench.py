@@ -54,7 +54,8 @@ DESCRIPTION = {
 }
 # sources that decide the attention kernel's memory traffic (kernel, launch
 # shape, split and merge policy); the stored HBM counters hold for this hash
-ATTN_SOURCES = ("decode_attention_mfa_amd/csrc/mfa_attn.hip", "decode_attention_mfa_amd/csrc/mfa_device.h",
+ATTN_SOURCES = ("decode_attention_mfa_amd/csrc/mfa_attn.hip", "decode_attention_mfa_amd/csrc/mfa_attn_piece_setup.inc",
+                "decode_attention_mfa_amd/csrc/mfa_attn_piece_run.inc", "decode_attention_mfa_amd/csrc/mfa_device.h",
                 "decode_attention_mfa_amd/csrc/mfa_internal.h", "decode_attention_mfa_amd/csrc/mfa_api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WARMUP_SECONDS = 0.5
@@ -234,15 +235,16 @@ def main():
     # after the append the attention reads L_b + 1 rows
     attn_lens = dc.seq_lens + 1 if append else dc.seq_lens
     attn_max = dc.max_len + 1 if append else dc.max_len
+    attn_min = dc.min_len + 1 if append else dc.min_len
     h = harness.create_handle(dc, split_tokens=args.split, max_context=attn_max)
-    split = mfa.mfa_split_tokens(h, dc.batch, attn_max)
+    split = mfa.mfa_split_tokens(h, dc.batch, attn_max, attn_min)
     stream = torch.cuda.Stream()
     outs = [harness.alloc_outputs(dc) for _ in range(nrot)]
     qbufs = [torch.empty((dc.batch, 64, 256), dtype=torch.int16, device="cuda") for _ in range(nrot)]
 
     kvs = [c.kv() for c in sets]
     attn_kvs = [mfa.make_kv(c.k, c.v, attn_lens, page_table=c.page_table, k_scale=c.k_scale,
-                            v_scale=c.v_scale, max_seq_len=attn_max) for c in sets]
+                            v_scale=c.v_scale, max_seq_len=attn_max, min_seq_len=attn_min) for c in sets]
 
     def step(i):
         s = sets[i % nrot]
@@ -304,9 +306,11 @@ def main():
                    "context_min": int(case.seq_lens.min()), "context_max": int(case.seq_lens.max()),
                    "kv_dtype": "fp8_e4m3" if case.kv_dtype == "fp8" else "bf16",
                    "layout": "paged64" if case.paged else "contiguous", "split_tokens": split,
+                   "work_split": "balanced ranges of steps" if split == 0 else f"chunks of {split} tokens",
                    "input_sets_rotated": nrot, "mall": "cold" if cold else "warm"},
         "step_hbm_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": "mfa_attn_split_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "mfa_attn_balanced_kernel" if split == 0 else "mfa_attn_split_kernel",
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": attn_bytes,
                      "avg_launch_us": round(attn_ms * 1e3, 2), "source_sha": sha,

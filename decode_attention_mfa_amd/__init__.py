@@ -23,6 +23,7 @@ MFA_ERR_NOMEM = -3
 MFA_ERR_HIP = -4
 MFA_DTYPE_BF16 = 0
 MFA_DTYPE_FP8_E4M3 = 1
+MFA_SPLIT_BALANCED = -1
 KERNEL_KINDS = ("attention", "combine", "qproj_down", "rmsnorm", "qproj_up", "kv_proj", "kv_write")
 
 
@@ -46,7 +47,8 @@ class mfa_kv(ctypes.Structure):
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("seq_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
                 ("pt_stride", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("kv_stride", ctypes.c_int64), ("max_seq_len", ctypes.c_int32)]
+                ("kv_stride", ctypes.c_int64), ("max_seq_len", ctypes.c_int32),
+                ("min_seq_len", ctypes.c_int32)]
 
 
 def _load_lib():
@@ -64,7 +66,7 @@ def _load_lib():
     lib.mfa_kv_append.argtypes = [P, P, P, P, ctypes.POINTER(mfa_kv), I32, P]
     lib.mfa_kv_append.restype = ctypes.c_int
     lib.mfa_decode.restype = ctypes.c_int
-    lib.mfa_split_tokens.argtypes = [P, I32, I32]
+    lib.mfa_split_tokens.argtypes = [P, I32, I32, I32]
     lib.mfa_split_tokens.restype = I32
     lib.mfa_debug_gather_kv.argtypes = [P, ctypes.POINTER(mfa_kv), I32, P, P, P]
     lib.mfa_debug_gather_kv.restype = ctypes.c_int
@@ -125,7 +127,7 @@ def make_config(*, hidden=7168, q_rank=2048, num_heads=64, head_dim=256, kv_dtyp
 
 
 def make_kv(k, v, seq_lens, *, page_table=None, k_scale=1.0, v_scale=1.0, kv_stride=0,
-            pt_stride=0, num_pages=0, max_seq_len=0) -> mfa_kv:
+            pt_stride=0, num_pages=0, max_seq_len=0, min_seq_len=0) -> mfa_kv:
     """Describe a KV cache. For torch tensors the strides default from the
     shapes: contiguous k [B, S, 256] -> kv_stride S; paged k [P, 64, 256] ->
     num_pages P; page_table [B, n] -> pt_stride n."""
@@ -137,7 +139,7 @@ def make_kv(k, v, seq_lens, *, page_table=None, k_scale=1.0, v_scale=1.0, kv_str
     elif not kv_stride and hasattr(k, "shape"):
         kv_stride = int(k.shape[1])
     return mfa_kv(_ptr(k), _ptr(v), k_scale, v_scale, _ptr(seq_lens), _ptr(page_table),
-                  pt_stride, num_pages, kv_stride, max_seq_len)
+                  pt_stride, num_pages, kv_stride, max_seq_len, min_seq_len)
 
 
 def mfa_create(cfg: Optional[mfa_config] = None, **kw) -> int:
@@ -165,8 +167,8 @@ def mfa_kv_append(h: int, x, w_k, w_v, kv: mfa_kv, batch: int, stream=None) -> N
                              _stream(stream)), "mfa_kv_append")
 
 
-def mfa_split_tokens(h: int, batch: int, max_seq_len: int = 0) -> int:
-    return _check(lib.mfa_split_tokens(h, batch, max_seq_len), "mfa_split_tokens")
+def mfa_split_tokens(h: int, batch: int, max_seq_len: int = 0, min_seq_len: int = 0) -> int:
+    return _check(lib.mfa_split_tokens(h, batch, max_seq_len, min_seq_len), "mfa_split_tokens")
 
 
 def mfa_debug_gather_kv(h: int, kv: mfa_kv, b: int, k_dst, v_dst, stream=None) -> None:

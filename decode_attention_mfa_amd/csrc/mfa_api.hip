@@ -100,6 +100,20 @@ static int32_t kv_ksplit(int32_t hidden, int32_t batch) {
     return hidden / rows;
 }
 
+// Balanced work split (equal step ranges per workgroup) when the caller asks
+// for it, or by default for batches of at least half a workgroup per CU
+// (there every sequence spans few ranges, so the last range of a sequence to
+// finish merges its pieces cheaply) unless the caller's length bounds show
+// that every sequence has the same number of 64-token steps: then equal
+// chunks are already balanced and need no length scan. Smaller batches of
+// long sequences keep per-sequence chunks and the separate merge kernel.
+static bool use_balanced(const mfa_ctx* h, int32_t batch, int32_t max_len, int32_t min_len) {
+    if (h->cfg.split_tokens == MFA_SPLIT_BALANCED) return true;
+    if (h->cfg.split_tokens != 0 || 2 * batch < h->num_cu) return false;
+    const bool uniform = min_len > 0 && (min_len + mfa::kStep - 1) / mfa::kStep == (max_len + mfa::kStep - 1) / mfa::kStep;
+    return !uniform;
+}
+
 static int32_t choose_split(const mfa_ctx* h, int32_t batch, int32_t max_len) {
     if (h->cfg.split_tokens > 0) return h->cfg.split_tokens;
     if (max_len <= 0) return kMinAutoSplit;
@@ -147,8 +161,9 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
         return fail(MFA_ERR_UNSUPPORTED, "mfa_create: page_size must be 0 or 64 (got %d)", c.page_size);
     if (c.max_batch < 1 || c.max_context < 1)
         return fail(MFA_ERR_INVALID, "mfa_create: max_batch and max_context must be >= 1");
-    if (c.split_tokens < 0 || c.split_tokens % mfa::kStep != 0)
-        return fail(MFA_ERR_INVALID, "mfa_create: split_tokens must be 0 or a positive multiple of 64 (got %d)",
+    if (c.split_tokens < MFA_SPLIT_BALANCED || (c.split_tokens > 0 && c.split_tokens % mfa::kStep != 0))
+        return fail(MFA_ERR_INVALID,
+                    "mfa_create: split_tokens must be 0, MFA_SPLIT_BALANCED or a positive multiple of 64 (got %d)",
                     c.split_tokens);
     if (c.page_size != 0 && c.split_tokens > mfa::kMaxPagedChunkSteps * mfa::kStep)
         return fail(MFA_ERR_UNSUPPORTED, "mfa_create: with a paged cache split_tokens must be <= %d (got %d)",
@@ -160,7 +175,9 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
 
     const int min_chunk = c.split_tokens > 0 ? c.split_tokens : kMinAutoSplit;
     const int64_t max_chunks = ((int64_t)c.max_context + min_chunk - 1) / min_chunk;
-    const int64_t nparts = (int64_t)c.max_batch * max_chunks;
+    // one more slot per sequence than chunks: a balanced split may cut a
+    // sequence into ceil(steps / 4) + 1 pieces
+    const int64_t nparts = (int64_t)c.max_batch * (max_chunks + 1);
     const int64_t bytes_o = nparts * mfa::kHeads * mfa::kHeadDim * 4;
     const int64_t bytes_lse = nparts * mfa::kHeads * 4;
     const int64_t bytes_c = (int64_t)(c.hidden / mfa::kQprojRowsPerSplit) * c.max_batch * c.q_rank * 4;
@@ -226,9 +243,10 @@ int mfa_destroy(mfa_handle h) {
     return MFA_OK;
 }
 
-int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len) {
+int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len) {
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_split_tokens: not a live handle");
     if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;
+    if (use_balanced(h, batch, max_seq_len, min_seq_len)) return 0;
     return choose_split(h, batch, max_seq_len);
 }
 
@@ -321,20 +339,39 @@ int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* 
     a.part_o = h->part_o;
     a.part_lse = h->part_lse;
     a.counters = h->counters;
-    a.chunk = choose_split(h, batch, max_len);
-    a.n_chunk = (max_len + a.chunk - 1) / a.chunk;
-    if (a.n_chunk < 1) a.n_chunk = 1;
-    if (a.n_chunk > h->max_chunks)
-        return fail(MFA_ERR_INVALID, "mfa_decode: %d chunks exceed the workspace (%d)", a.n_chunk, h->max_chunks);
-    a.fuse_max = a.n_chunk <= mfa::kFusedMaxChunks ? mfa::kFusedMaxChunks : 1;
+    a.batch = batch;
+    int workgroups;
+    if (use_balanced(h, batch, max_len, kv->min_seq_len)) {
+        // equal ranges of at least 4 and at most 128 steps: one workgroup per
+        // CU, or more when the batch's steps could exceed 128 per workgroup
+        a.balanced = 1;
+        a.chunk = 0;
+        a.n_chunk = 0;
+        a.part_stride = h->max_chunks + 1;
+        a.fuse_max = 1 << 30;   // the last piece of a sequence always merges
+        const int64_t bound = (int64_t)batch * ((max_len + mfa::kStep - 1) / mfa::kStep);
+        int64_t g = h->num_cu;
+        if (bound > g * mfa::kMaxPagedChunkSteps) g = round_up((bound + mfa::kMaxPagedChunkSteps - 1) / mfa::kMaxPagedChunkSteps, h->num_cu);
+        workgroups = (int)g;
+    } else {
+        a.balanced = 0;
+        a.chunk = choose_split(h, batch, max_len);
+        a.n_chunk = (max_len + a.chunk - 1) / a.chunk;
+        if (a.n_chunk < 1) a.n_chunk = 1;
+        if (a.n_chunk > h->max_chunks)
+            return fail(MFA_ERR_INVALID, "mfa_decode: %d chunks exceed the workspace (%d)", a.n_chunk, h->max_chunks);
+        a.part_stride = a.n_chunk;
+        a.fuse_max = a.n_chunk <= mfa::kFusedMaxChunks ? mfa::kFusedMaxChunks : 1;
+        workgroups = batch * a.n_chunk;
+    }
     const float log2e = 1.4426950408889634f;
     a.score_scale = h->cfg.softmax_scale * (fp8 ? kv->k_scale : 1.0f) * log2e;
     a.v_scale = fp8 ? kv->v_scale : 1.0f;
     hipStream_t st = (hipStream_t)hip_stream;
     const bool paged = h->cfg.page_size != 0;
     hipError_t e = timed_launch(h, MFA_KERNEL_ATTENTION, st,
-                                [&](const mfa::Launch& l) { return mfa::launch_attn_split(a, fp8, paged, batch, l); });
-    if (e == hipSuccess && a.n_chunk > a.fuse_max)
+                                [&](const mfa::Launch& l) { return mfa::launch_attn_split(a, fp8, paged, workgroups, l); });
+    if (e == hipSuccess && !a.balanced && a.n_chunk > a.fuse_max)
         e = timed_launch(h, MFA_KERNEL_COMBINE, st, [&](const mfa::Launch& l) { return mfa::launch_combine(a, batch, l); });
     if (e != hipSuccess) return hip_fail(e, "mfa_decode: launch");
     return MFA_OK;

@@ -5,8 +5,11 @@
 // log-sum-exp identity (Flash-Decoding, cited by title on the DeepSeek-V4
 // references).
 //
-// One workgroup (4 wave64s) owns one (sequence, chunk). It walks the chunk in
-// steps of 64 tokens (= one cache page):
+// One workgroup (4 wave64s) owns a piece of one sequence: a chunk (chunked
+// kernel) or the part of its equal range of the batch's steps that falls in
+// that sequence (balanced kernel; see the notes before the two kernels). The
+// piece body (mfa_attn_piece_setup.inc, mfa_attn_piece_run.inc) walks the
+// piece in steps of 64 tokens (= one cache page):
 //   load  K and V rows of a step go from HBM straight into an LDS ring slot
 //         (global_load_lds_dwordx4, no registers); FP8 keeps 4 steps in
 //         flight, bf16 2. Wave w fetches rows 16w..16w+15 of both tensors.
@@ -26,11 +29,11 @@
 // One workgroup barrier per step orders the ring, P and the vote.
 //
 // Scores are kept in the base-2 domain: s2 = s * log2(e), exp -> exp2.
-// Output of a chunk: for a one-chunk sequence the final bf16 output and lse;
-// otherwise the chunk-normalised output (fp32) and its base-2 lse, merged by
-// the log-sum-exp identity either here, by the last of the sequence's chunks
-// to finish (launches where no sequence has more than two chunks), or by
-// mfa_combine_kernel afterwards.
+// Output of a piece: for a one-piece sequence the final bf16 output and lse;
+// otherwise the piece-normalised output (fp32) and its base-2 lse, merged by
+// the log-sum-exp identity either here, by the last of the sequence's pieces
+// to finish (balanced launches, and chunked launches where no sequence has
+// more than two chunks), or by mfa_combine_kernel afterwards.
 #include <type_traits>
 
 #include "mfa_device.h"
@@ -125,38 +128,29 @@ __device__ __forceinline__ void wait_vmem() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+
+// ------------------------------------------------------------ the two kernels
+// Two ways to cut the work into workgroups:
+//   chunks   (mfa_attn_split_kernel): workgroup (b, c) takes tokens
+//            [c*chunk, (c+1)*chunk) of sequence b; workgroups past L_b exit.
+//   balanced (mfa_attn_balanced_kernel): the 64-token steps of all sequences,
+//            in sequence order, are dealt out in equal ranges of `per` steps
+//            (per = ceil(total / workgroups), at least kMinBalancedSteps, at
+//            most kMaxPagedChunkSteps), so every workgroup streams the same
+//            number of bytes whatever the lengths (the work-centric
+//            decomposition of Stream-K, cited by title on the DeepSeek-V4
+//            references, applied to KV steps). A range may hold the end of one
+//            sequence and the start of others; each piece is a call of
+//            attend_piece, and the last of a sequence's pieces to finish
+//            merges them.
+// Both run the same piece body (the two .inc files).
+
 template <bool FP8, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mfa_attn_split_kernel(const AttnArgs p) {
-    constexpr int ELEM = FP8 ? 1 : 2;
-    constexpr int ROWB = kHeadDim * ELEM;          // bytes per cached row
-    constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
-    constexpr int RPI = 1024 / ROWB;               // rows per 1 KB DMA instruction
-    constexpr int KW = 16 * ROWB;                  // a wave's 16 rows of one step
-    constexpr int VT = kStep * ROWB;               // the V tile of one step
-    constexpr int NDMA = KW / 1024;                // DMA instructions per wave for K (same for V)
-    constexpr int OPS = 2 * NDMA;                  // vector-memory instructions per wave per step
-    // steps in flight: 4 x 32 KB (FP8) or 2 x 64 KB (bf16) of K + V
-    constexpr int RING = FP8 ? 4 : 2;
-
-    // LDS: the ring (slot-major: four waves' K rows, then the V tile), then
-    // the two P buffers. Slot RING-1 doubles as the staging area for Q.
-    constexpr int SLOT = 4 * KW + VT;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[RING * SLOT + 2 * kHeads * kStep * 2];
-    __shared__ __attribute__((aligned(16))) float xchg[4][kHeads];
-    __shared__ __attribute__((aligned(16))) float xchg2[4][kHeads];
-    __shared__ int flags_all[2][4];
-    __shared__ int arrival;
-    __shared__ float lse_lds[kHeads];
-    auto kring = [&](int slot, int wave) -> uint8_t* { return smem + slot * SLOT + wave * KW; };
-    auto vring = [&](int slot) -> uint8_t* { return smem + slot * SLOT + 4 * KW; };
-    auto plds_of = [&](int parity) -> uint8_t* { return smem + RING * SLOT + parity * (kHeads * kStep * 2); };
-
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l = tid & 63;
-    const int lr = l & 15;
-    const int g = l >> 4;
+#define MFA_PIECE_TID threadIdx.x
+#include "mfa_attn_piece_setup.inc"
+#undef MFA_PIECE_TID
 
     const int b = blockIdx.x / p.n_chunk;
     const int c = blockIdx.x - b * p.n_chunk;
@@ -178,510 +172,160 @@ void mfa_attn_split_kernel(const AttnArgs p) {
     const int last_s = nsteps - 1;
     const bool single = (L + p.chunk - 1) / p.chunk == 1;
 
-    // ---- DMA lane offsets (bytes from the step's first row; loop-invariant).
-    // Instruction i of wave w fills rows 16w + RPI*i + l/CPR; lane l lands at
-    // chunk position l % CPR of its row and so fetches the data chunk that the
-    // swizzle puts there.
-    uint32_t koff[NDMA], voff[NDMA];
-#pragma unroll
-    for (int i = 0; i < NDMA; i++) {
-        const int t = RPI * i + l / CPR;           // row within the wave's 16
-        const int r = 16 * w + t;                  // row within the step
-        koff[i] = r * ROWB + 16 * ((l % CPR) ^ kswz(t));
-        voff[i] = r * ROWB + 16 * ((l % CPR) ^ vswz<FP8>(r));
-    }
-
-    // ---- paged caches: the pages of the chunk's steps, fetched once. Lane j
-    // holds the page of step j (pg0) and of step 64 + j (pg1); a step reads
-    // its page with v_readlane, so no load (and no wait for one) sits in the
-    // loop. Paged chunks have at most kMaxPagedChunkSteps = 128 steps (the
-    // host enforces it).
-    int32_t pg0 = 0, pg1 = 0;
-    if constexpr (PAGED) {
-        const int32_t* chunk_pt = p.kv.page_table + (int64_t)b * p.kv.pt_stride + (t_begin >> 6);
-        if (l < nsteps) pg0 = chunk_pt[l];
-        if (64 + l < nsteps) pg1 = chunk_pt[64 + l];
-    }
-    // first cache row of step s (s <= last_s)
-    auto step_row = [&](int s) -> int64_t {
-        if constexpr (PAGED) {
-            const int32_t page = s < 64 ? __builtin_amdgcn_readlane(pg0, s) : __builtin_amdgcn_readlane(pg1, s - 64);
-            return (int64_t)page * kPage;
-        } else {
-            return kv_step_base<false>(p.kv, b, t_begin + s * kStep);
-        }
-    };
-
-    // ---- issue the loads of step s (clamped to the last step, whose rows then
-    // hit in L2) into ring slot s % RING: this wave's 16 K rows into its
-    // private region, and the same 16 rows of V into the shared V tile.
-    auto issue_step = [&](int s) {
-        const int t0 = t_begin + min(s, last_s) * kStep;
-        const int64_t base = step_row(min(s, last_s));
-        const uint8_t* kb = wave_uniform(p.kv.k + base * ROWB);
-        const uint8_t* vb = wave_uniform(p.kv.v + base * ROWB);
-        const int slot = s % RING;
-        const uint32_t kd = __builtin_amdgcn_readfirstlane(lds_addr(kring(slot, w)));
-        const uint32_t vd = __builtin_amdgcn_readfirstlane(lds_addr(vring(slot)) + 16 * w * ROWB);
-        const int last = t_end - 1 - t0;           // last valid row of the step
-        if (last >= kStep - 1) {
-#pragma unroll
-            for (int i = 0; i < NDMA; i++) {
-                dma_b128(kb, koff[i], kd + 1024 * i);
-                dma_b128(vb, voff[i], vd + 1024 * i);
-            }
-        } else {   // partial last step: rows past the chunk end repeat the last row
-#pragma unroll
-            for (int i = 0; i < NDMA; i++) {
-                const int r = 16 * w + RPI * i + l / CPR;
-                const uint32_t shift = (uint32_t)((min(r, last) - r) * ROWB);
-                dma_b128(kb, koff[i] + shift, kd + 1024 * i);
-                dma_b128(vb, voff[i] + shift, vd + 1024 * i);
-            }
-        }
-    };
-
-    // ---- Q, fetched once per workgroup by DMA into the staging area (slot
-    // RING-1 of the ring, free until the first step's barrier): 16-byte
-    // chunk c of head h at position c ^ (h & 15); wave w copies heads
-    // 16w..16w+15. The ring's first steps stream in behind it.
-    uint8_t* const qs = smem + (RING - 1) * SLOT;
-    {
-        const uint8_t* qb = wave_uniform(reinterpret_cast<const uint8_t*>(p.q + (int64_t)b * kHeads * kHeadDim));
-        const uint32_t qd = __builtin_amdgcn_readfirstlane(lds_addr(qs + 16 * w * 512));
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int h = 16 * w + 2 * i + (l >> 5);
-            dma_b128(qb, (uint32_t)(h * 512 + 16 * ((l & 31) ^ (h & 15))), qd + 1024 * i);
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < RING - 1; s++) issue_step(s);
-
-    // Every wave reads its B operands: qop[ht][ks] holds Q[16ht + lr][d(ks,
-    // g, 0..7)] with d(ks, g, j) = 64*(ks/2) + 16*g + 8*(ks%2) + j, the same
-    // d order the K A operands use below.
-    bf16x8 qop[4][8];
-    {
-        // this wave's Q rows have landed once at most the ring's loads are in
-        // flight; the barrier makes every wave's rows visible
-        wait_vmem<(RING - 1) * OPS>();
-        lds_barrier();
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++)
-#pragma unroll
-            for (int ks = 0; ks < 8; ks++) {
-                const int h = 16 * ht + lr;
-                const int cq = 8 * (ks >> 1) + 2 * g + (ks & 1);
-                qop[ht][ks] = *reinterpret_cast<const bf16x8*>(qs + h * 512 + 16 * (cq ^ (h & 15)));
-            }
-    }
-
-    // ---- per-pass state (QK layout: heads 16ht + lr). The reference maxima
-    // are fixed for a whole pass over the chunk: the exact maxima of the
-    // first step, raised to m_floor. A later score may exceed its reference
-    // by up to kTau (base 2), so unnormalised P <= 2^kTau and the output
-    // accumulators are never rescaled inside the loop. A larger excess, voted
-    // by any wave, restarts the chunk with the floor raised.
-    float mq[4];         // reference maxima (base 2)
-    float lq[4];         // partial softmax denominators of the rounded P
-    float le[4];         // partial softmax denominators of the unrounded P
-    float m_floor[4];    // lower bound for the references (from a restart)
-    f32x4 o[4][4];       // O[16ht + 4g + i][64w + 16dt + lr]
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++) m_floor[ht] = -__builtin_inff();
-
-    auto clear_acc = [&]() {
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            lq[ht] = 0.f;
-            le[ht] = 0.f;
-#pragma unroll
-            for (int dt = 0; dt < 4; dt++) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    };
-
-    // scores S^T[token 4g+i][head 16ht+lr] of this wave's 16 tokens of step s
-    // (its K rows have landed), tokens past the chunk end at -inf
-    auto qk = [&](int s, f32x4* sc) {
-        const int t0 = t_begin + s * kStep;
-        const uint8_t* klds = kring(s % RING, w) + lr * ROWB;   // this lane's K row
-        u32x4 kp[FP8 ? 4 : 8];
-#pragma unroll
-        for (int i = 0; i < (FP8 ? 4 : 8); i++) {
-            // fp8: piece i = bytes 64i + 16g; bf16: bytes 128(i/2) + 32g + 16(i%2)
-            const int cidx = FP8 ? (4 * i + g) : (8 * (i >> 1) + 2 * g + (i & 1));
-            kp[i] = *reinterpret_cast<const u32x4*>(klds + 16 * (cidx ^ kswz(lr)));
-        }
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) sc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP8) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const bf16x8 a0 = e4m3x8_to_bf16x8(kp[i].x, kp[i].y);
-                const bf16x8 a1 = e4m3x8_to_bf16x8(kp[i].z, kp[i].w);
-#pragma unroll
-                for (int ht = 0; ht < 4; ht++) {
-                    sc[ht] = mfma16(a0, qop[ht][2 * i], sc[ht]);
-                    sc[ht] = mfma16(a1, qop[ht][2 * i + 1], sc[ht]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 8; ks++) {
-                const bf16x8 a = bitcast<bf16x8>(kp[ks]);
-#pragma unroll
-                for (int ht = 0; ht < 4; ht++) sc[ht] = mfma16(a, qop[ht][ks], sc[ht]);
-            }
-        }
-        if (t_end - t0 < kStep) {   // last step of the chunk only
-            const int valid = t_end - t0 - (16 * w + 4 * g);   // rows i < valid are real tokens
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++)
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    if (i >= valid) sc[ht][i] = -__builtin_inff();
-        }
-    };
-
-    // per-head maxima (base 2) of this step over all four waves, in QK layout
-    auto exchange_max = [&](const f32x4* sc, float* m_out) {
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            float m = fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3]));
-            m = fmaxf(m, __shfl_xor(m, 16));
-            m = fmaxf(m, __shfl_xor(m, 32));
-            if (g == 0) lds_store_b32(&xchg[w][16 * ht + lr], __builtin_bit_cast(uint32_t, m * p.score_scale));
-        }
-        lds_barrier();
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            const int h = 16 * ht + lr;
-            m_out[ht] = fmaxf(fmaxf(xchg[0][h], xchg[1][h]), fmaxf(xchg[2][h], xchg[3][h]));
-        }
-    };
-
-    // P = exp2(s2 - reference), rounded to bf16, into the step's P buffer.
-    // Two partial denominators: of the rounded P (normalises the output, so
-    // the weights applied to V sum to one) and of the unrounded P (gives the
-    // log-sum-exp to fp32 accuracy instead of bf16's 2^-8).
-    auto write_p = [&](int s, const f32x4* sc, float* lr_step, float* le_step) {
-        uint8_t* plds = plds_of(s & 1);
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            float e[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ht][i], p.score_scale, -mq[ht]));
-            const uint32_t p01 = pack_bf16x2(e[0], e[1]);
-            const uint32_t p23 = pack_bf16x2(e[2], e[3]);
-            lr_step[ht] = (__builtin_bit_cast(float, p01 << 16) + __builtin_bit_cast(float, p01 & 0xffff0000u)) +
-                          (__builtin_bit_cast(float, p23 << 16) + __builtin_bit_cast(float, p23 & 0xffff0000u));
-            le_step[ht] = (e[0] + e[1]) + (e[2] + e[3]);
-            const int h = 16 * ht + lr;
-            const int ch = (2 * w + (g >> 1)) ^ pswz(h);
-            lds_store_b64(plds + h * 128 + 16 * ch + 8 * (g & 1), u32x2{p01, p23});
-        }
-    };
-
-    // O[64 heads][64w..64w+63] += P[64 x 64 tok] . V[64 tok x 64w..64w+63];
-    // all LDS reads of the step are issued before the conversions and MFMAs
-    auto pv = [&](int s) {
-        const uint8_t* plds = plds_of(s & 1);
-        const uint8_t* vt = vring(s % RING);
-        bf16x8 pa[2][4];
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) {
-                const int h = 16 * ht + lr;
-                pa[kk][ht] = *reinterpret_cast<const bf16x8*>(plds + h * 128 + 16 * ((4 * kk + g) ^ pswz(h)));
-            }
-        if constexpr (FP8) {
-            // lane j of a 16-lane group points at row r0 + j/2, bytes 8(j%2)..+7
-            // of chunk 4w + dt; it receives column 64w + 16dt + j of rows r0..r0+7
-            i32x2 vr[2][4];
-#pragma unroll
-            for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++) {
-                    const int row = 32 * kk + 8 * g + (lr >> 1);
-                    const uint8_t* a = vt + row * ROWB + 16 * ((4 * w + dt) ^ vswz<FP8>(row)) + 8 * (lr & 1);
-                    vr[kk][dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (__attribute__((address_space(3))) i32x2*)(a));
-                }
-#pragma unroll
-            for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++) {
-                    const bf16x8 vb = e4m3x8_to_bf16x8((uint32_t)vr[kk][dt].x, (uint32_t)vr[kk][dt].y);
-#pragma unroll
-                    for (int ht = 0; ht < 4; ht++) o[ht][dt] = mfma16(pa[kk][ht], vb, o[ht][dt]);
-                }
-        } else {
-            // two transposed reads of 4 rows each: lane j points at row
-            // r0 + j/4, elements 4(j%4)..+3 of the 16-column block
-            i16x4 vr[2][4][2];
-#pragma unroll
-            for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-                    for (int hh = 0; hh < 2; hh++) {
-                        const int row = 32 * kk + 8 * g + 4 * hh + (lr >> 2);
-                        const int ch = 8 * w + 2 * dt + ((lr & 3) >> 1);
-                        const uint8_t* a = vt + row * ROWB + 16 * (ch ^ vswz<FP8>(row)) + 8 * (lr & 1);
-                        vr[kk][dt][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(a));
-                    }
-#pragma unroll
-            for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++) {
-                    const u32x2 u0 = bitcast<u32x2>(vr[kk][dt][0]);
-                    const u32x2 u1 = bitcast<u32x2>(vr[kk][dt][1]);
-                    const bf16x8 vb = bitcast<bf16x8>(u32x4{u0.x, u0.y, u1.x, u1.y});
-#pragma unroll
-                    for (int ht = 0; ht < 4; ht++) o[ht][dt] = mfma16(pa[kk][ht], vb, o[ht][dt]);
-                }
-        }
-    };
-
-    // Step s > 0 against the fixed references. Returns true (in every wave)
-    // when some score exceeded its reference by more than kTau; m_floor then
-    // holds the raised bound and the step's P.V is skipped.
-    auto step = [&](int s) -> bool {
-        // this wave's K and V rows of step s have landed once at most the
-        // RING-2 younger steps' loads are in flight
-        wait_vmem<(RING - 2) * OPS>();
-        f32x4 sc[4];
-        qk(s, sc);
-        bool over = false;
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            const float m = fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3]));
-            over |= m * p.score_scale > mq[ht] + kTau;
-        }
-        const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
-        float lstep[4], estep[4];
-        write_p(s, sc, lstep, estep);
-        int* flags = flags_all[s & 1];
-        if (l == 0) lds_store_b32(&flags[w], wave_over ? 1u : 0u);
-        // after this barrier: P of step s and every wave's V rows of step s
-        // are visible, and every wave is done with the P.V of step s-1
-        lds_barrier();
-        if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
-            float m[4];
-            exchange_max(sc, m);
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) m_floor[ht] = fmaxf(mq[ht], m[ht]);
-            lds_barrier();   // everyone has read xchg before it is reused
-            // The next pass starts from zero. Clearing here (not at the top
-            // of the pass) leaves the accumulators entering this step with a
-            // single use, the P.V MFMA, so it can accumulate in place.
-            clear_acc();
-            return true;
-        }
-        // ring slot (s-1) % RING is free now: refill it
-        issue_step(s + RING - 1);
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            lq[ht] += lstep[ht];
-            le[ht] += estep[ht];
-        }
-        pv(s);
-        return false;
-    };
-
-    clear_acc();
-    for (int pass = 0;; pass++) {   // one pass over the chunk; repeated only after a vote
-        // Loads are issued unconditionally (past the last step they repeat
-        // its rows) so that every wait sees the same number of younger loads.
-        if (pass > 0) {
-#pragma unroll
-            for (int s = 0; s < RING - 1; s++) issue_step(s);
-        }
-        {   // step 0 sets the references from its exact maxima
-            wait_vmem<(RING - 2) * OPS>();
-            f32x4 sc[4];
-            qk(0, sc);
-            float m[4];
-            exchange_max(sc, m);
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) mq[ht] = fmaxf(m_floor[ht], m[ht]);
-            float lstep[4], estep[4];
-            write_p(0, sc, lstep, estep);
-            lds_barrier();
-            issue_step(RING - 1);
-#pragma unroll
-            for (int ht = 0; ht < 4; ht++) {
-                lq[ht] += lstep[ht];
-                le[ht] += estep[ht];
-            }
-            pv(0);
-        }
-        bool restart = false;
-        for (int s = 1; s < nsteps; s++)
-            if ((restart = step(s))) break;
-        // drain the ring's loads (the repeated ones too) before the next pass
-        // or the exit
-        wait_vmem<0>();
-        if (!restart) break;
-        lds_barrier();   // no wave still reads the ring or P of the pass
-    }
-
-    // ---- denominators: lanes -> wave (xor over g) -> workgroup (LDS)
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++) {
-        float v = lq[ht], u = le[ht];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        u += __shfl_xor(u, 16);
-        u += __shfl_xor(u, 32);
-        lq[ht] = v;
-        le[ht] = u;
-    }
-    __syncthreads();   // all waves are done with xchg
-    if (g == 0) {
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            xchg[w][16 * ht + lr] = lq[ht];
-            xchg2[w][16 * ht + lr] = le[ht];
-        }
-    }
-    __syncthreads();
-
-    // log-sum-exp (base 2) per head, from the QK layout of wave 0, shared
-    // through LDS
-    if (w == 0 && g == 0) {
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++) {
-            const int h = 16 * ht + lr;
-            const float lsum = ((xchg2[0][h] + xchg2[1][h]) + xchg2[2][h]) + xchg2[3][h];
-            lse_lds[h] = mq[ht] + __builtin_amdgcn_logf(lsum);   // v_log_f32 is log2
-        }
-    }
-    __syncthreads();
-
-    const int col = 64 * w + lr;
-    // this chunk's normalised output, PV layout
-#pragma unroll
-    for (int ht = 0; ht < 4; ht++) {
-        const int h0 = 16 * ht + 4 * g;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&xchg[0][h0]);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&xchg[1][h0]);
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&xchg[2][h0]);
-        const f32x4 l3 = *reinterpret_cast<const f32x4*>(&xchg[3][h0]);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float inv = p.v_scale / (((l0[i] + l1[i]) + l2[i]) + l3[i]);
-#pragma unroll
-            for (int dt = 0; dt < 4; dt++) o[ht][dt][i] *= inv;
-        }
-    }
-    auto store_final = [&](int h, int dt, float v) {
-        p.out[((int64_t)b * kHeads + h) * kHeadDim + col + 16 * dt] = bitcast<uint16_t>((__bf16)v);
-    };
-    if (single) {
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++) store_final(16 * ht + 4 * g + i, dt, o[ht][dt][i]);
-        if (p.lse_out && tid < kHeads) p.lse_out[b * kHeads + tid] = lse_lds[tid] * kLn2;
-        return;
-    }
-
-    // several chunks: publish this chunk's partial (normalised output and
-    // base-2 log-sum-exp)
-    const int64_t pidx = (int64_t)b * p.n_chunk + c;
-    const int nc = (L + p.chunk - 1) / p.chunk;
-    if (nc > p.fuse_max) {   // mfa_combine_kernel merges these after this kernel
-#pragma unroll
-        for (int ht = 0; ht < 4; ht++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                float* prow = p.part_o + (pidx * kHeads + 16 * ht + 4 * g + i) * kHeadDim + col;
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++) prow[16 * dt] = o[ht][dt][i];
-            }
-        if (tid < kHeads) p.part_lse[pidx * kHeads + tid] = lse_lds[tid];
-        return;
-    }
-
-    // few chunks: the workgroup that finishes a sequence's chunks last merges
-    // them. Each workgroup dumps its registers (thread-major: float4 j of
-    // thread tid at (j * 256 + tid), so every instruction writes 4 KB
-    // contiguous) with device-coherent stores that bypass the per-XCD L2;
-    // they are acknowledged (vmcnt 0) before the arrival count. The merging
-    // workgroup reads the other dumps back the same way after seeing the
-    // count. No cache-wide writeback or invalidate is needed.
-    f32x4* dump = reinterpret_cast<f32x4*>(p.part_o) + pidx * (kHeads * kHeadDim / 4);
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const int ht = j >> 2, i = j & 3;
-        coherent_store_b128(dump + j * 256 + tid, f32x4{o[ht][0][i], o[ht][1][i], o[ht][2][i], o[ht][3][i]});
-    }
-    if (tid < kHeads)
-        __hip_atomic_store(p.part_lse + pidx * kHeads + tid, lse_lds[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_vmem<0>();
-    __syncthreads();
-    if (tid == 0) arrival = __hip_atomic_fetch_add(&p.counters[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (arrival != nc - 1) return;
-    if (tid == 0) __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-    // chunks in index order whichever workgroup merges, so the result does
-    // not depend on which one finished last
-    const int64_t base = (int64_t)b * p.n_chunk;
-    float M[16], wsum[16];
-    f32x4 acc[16];
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        M[j] = -__builtin_inff();
-        wsum[j] = 0.f;
-        acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int cc = 0; cc < nc; cc++) {
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            const int h = 16 * (j >> 2) + 4 * g + (j & 3);
-            M[j] = fmaxf(M[j], __hip_atomic_load(p.part_lse + (base + cc) * kHeads + h, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT));
-        }
-    }
-    for (int cc = 0; cc < nc; cc++) {
-        f32x4 v[16];
-        if (cc == c) {   // this workgroup's own chunk, still in registers
-#pragma unroll
-            for (int j = 0; j < 16; j++) {
-                const int ht = j >> 2, i = j & 3;
-                v[j] = f32x4{o[ht][0][i], o[ht][1][i], o[ht][2][i], o[ht][3][i]};
-            }
-        } else {
-            const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o) + (base + cc) * (kHeads * kHeadDim / 4);
-            coherent_load_b128x8(v, src + tid, 256);
-            coherent_load_b128x8(v + 8, src + 8 * 256 + tid, 256);
-        }
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            const int h = 16 * (j >> 2) + 4 * g + (j & 3);
-            const float wc = __builtin_amdgcn_exp2f(
-                __hip_atomic_load(p.part_lse + (base + cc) * kHeads + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M[j]);
-            wsum[j] += wc;
-            acc[j] += wc * v[j];
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const int h = 16 * (j >> 2) + 4 * g + (j & 3);
-        const float inv = 1.f / wsum[j];
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) store_final(h, dt, acc[j][dt] * inv);
-        if (p.lse_out && w == 0 && lr == 0) p.lse_out[b * kHeads + h] = (M[j] + __builtin_amdgcn_logf(wsum[j])) * kLn2;
-    }
+#define MFA_PIECE_K c
+#define MFA_PIECE_NPARTS ((L + p.chunk - 1) / p.chunk)
+#define MFA_PIECE_BASE ((int64_t)b * p.n_chunk)
+#include "mfa_attn_piece_run.inc"
+#undef MFA_PIECE_K
+#undef MFA_PIECE_NPARTS
+#undef MFA_PIECE_BASE
 }
+
+// The thread index through an opaque copy: in the balanced kernel's piece
+// loop, values derived from it are then computed per piece instead of being
+// hoisted out of the loop, where they would stay live across the step loop.
+__device__ __forceinline__ int opaque_thread_index() {
+    int t;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+    return t;
+}
+
+// One piece of the balanced kernel: tokens [t_begin, t_end) of sequence b
+// (length L, t_begin < L), the piece_k-th of the sequence's nparts pieces,
+// whose partials sit at workspace slots part_base + 0 .. nparts-1.
+template <bool FP8, bool PAGED>
+__device__ __forceinline__ void attend_piece(const AttnArgs& p, const int b, const int L, const int t_begin,
+                                             const int t_end, const int piece_k, const int nparts,
+                                             const int64_t part_base) {
+#define MFA_PIECE_TID opaque_thread_index()
+#include "mfa_attn_piece_setup.inc"
+#undef MFA_PIECE_TID
+
+    const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
+    const int last_s = nsteps - 1;
+    const bool single = nparts == 1;
+
+#define MFA_PIECE_K piece_k
+#define MFA_PIECE_NPARTS nparts
+#define MFA_PIECE_BASE part_base
+#include "mfa_attn_piece_run.inc"
+#undef MFA_PIECE_K
+#undef MFA_PIECE_NPARTS
+#undef MFA_PIECE_BASE
+}
+
+// out = 0, lse = -inf for an empty sequence.
+__device__ __forceinline__ void write_empty(const AttnArgs& p, int b) {
+    uint16_t* ob = p.out + (int64_t)b * kHeads * kHeadDim;
+    for (int i = threadIdx.x; i < kHeads * kHeadDim / 8; i += 256)
+        reinterpret_cast<u32x4*>(ob)[i] = u32x4{0, 0, 0, 0};
+    if (p.lse_out && threadIdx.x < kHeads) p.lse_out[b * kHeads + threadIdx.x] = -__builtin_inff();
+}
+
+template <bool FP8, bool PAGED>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void mfa_attn_balanced_kernel(const AttnArgs p) {
+    __shared__ int wave_total[4];
+    __shared__ int first_seq[3];
+    __shared__ unsigned empty_mask;   // bit j: sequence blockIdx.x + j*G is empty
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int w = tid >> 6;
+    const int B = p.batch;
+    const int G = gridDim.x;
+    auto steps_of_len = [](int len) { return (len + kStep - 1) / kStep; };
+
+    // prefix of the step counts over sequences: thread t sums sequences
+    // [t*per_t, (t+1)*per_t) (up to four lengths kept in registers, so
+    // the lengths are read once), then a scan across the workgroup
+    constexpr int kRegLens = 4;
+    const int per_t = (B + 255) / 256;
+    const int b0 = min(B, tid * per_t), b1 = min(B, b0 + per_t);
+    int lens[kRegLens];
+    int cnt = 0;
+    if (tid == 0) empty_mask = 0;
+    __syncthreads();
+    // the lengths are read here only: the empty sequences this workgroup
+    // clears (b = blockIdx.x + j*G, j < 32) are noted in a mask
+    auto note_empty = [&](int bb, int len) {
+        if (len == 0 && bb % G == (int)blockIdx.x && bb / G < 32)
+            atomicOr(&empty_mask, 1u << (bb / G));
+    };
+    if (per_t <= kRegLens) {
+#pragma unroll
+        for (int i = 0; i < kRegLens; i++) {
+            lens[i] = b0 + i < b1 ? seq_len(p.kv, b0 + i) : 0;
+            cnt += steps_of_len(lens[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kRegLens; i++)
+            if (b0 + i < b1) note_empty(b0 + i, lens[i]);
+    } else {
+        for (int bb = b0; bb < b1; bb++) {
+            const int len = seq_len(p.kv, bb);
+            cnt += steps_of_len(len);
+            note_empty(bb, len);
+        }
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (l >= off) incl += v;
+    }
+    if (l == 63) wave_total[w] = incl;
+    __syncthreads();
+    int excl = incl - cnt;
+    for (int i = 0; i < w; i++) excl += wave_total[i];
+    const int total = ((wave_total[0] + wave_total[1]) + wave_total[2]) + wave_total[3];
+    const int per = min(kMaxPagedChunkSteps, max(kMinBalancedSteps, (total + G - 1) / G));
+    const int s_lo = blockIdx.x * per;
+    const int s_hi = min(total, s_lo + per);
+    if (s_lo < total) {
+        // the sequence holding step s_lo, its first step and its length
+        if (excl <= s_lo && s_lo < excl + cnt) {
+            int P = excl;
+            for (int bb = b0; bb < b1; bb++) {
+                const int len = per_t <= kRegLens ? lens[min(bb - b0, kRegLens - 1)] : seq_len(p.kv, bb);
+                const int n = steps_of_len(len);
+                if (s_lo < P + n) {
+                    first_seq[0] = bb;
+                    first_seq[1] = P;
+                    first_seq[2] = len;
+                    break;
+                }
+                P += n;
+            }
+        }
+        __syncthreads();
+        int bq = __builtin_amdgcn_readfirstlane(first_seq[0]);
+        int Pq = __builtin_amdgcn_readfirstlane(first_seq[1]);
+        int L = __builtin_amdgcn_readfirstlane(first_seq[2]);
+        for (int s = s_lo;;) {
+            const int n = steps_of_len(L);
+            if (n > 0) {
+                const int seg_end = min(s_hi, Pq + n);
+                const int first = Pq / per, last = (Pq + n - 1) / per;
+                attend_piece<FP8, PAGED>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
+                                         (int)blockIdx.x - first, last - first + 1, (int64_t)bq * p.part_stride);
+                s = seg_end;
+                if (s >= s_hi) break;
+                __syncthreads();   // the piece is done with the LDS
+            }
+            Pq += n;
+            bq++;
+            L = seq_len(p.kv, bq);
+        }
+    }
+    // empty sequences b = blockIdx.x (mod G): out = 0, lse = -inf (from
+    // the mask for the first 32, reading the length past that)
+    const unsigned em = __builtin_amdgcn_readfirstlane(*(volatile unsigned*)&empty_mask);
+    for (int j = 0; j < 32; j++)
+        if (em & (1u << j)) write_empty(p, (int)blockIdx.x + j * G);
+    for (int bb = (int)blockIdx.x + 32 * G; bb < B; bb += G)
+        if (seq_len(p.kv, bb) == 0) write_empty(p, bb);
+}
+
 
 // Merge the chunk partials of every sequence with more than one chunk:
 //   M = max_c lse2_c, W_c = 2^(lse2_c - M), out = sum_c W_c o_c / sum_c W_c,
@@ -761,8 +405,15 @@ __global__ __launch_bounds__(256) void mfa_gather_kernel(const KvView kv, int b,
     }
 }
 
-hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch, const Launch& l) {
-    const dim3 grid(batch * a.n_chunk), block(256);
+hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l) {
+    const dim3 grid(workgroups), block(256);
+    if (a.balanced) {
+        if (fp8)
+            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_balanced_kernel<true, false>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_balanced_kernel<false, true>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_balanced_kernel<false, false>, grid, block, l, a);
+    }
     if (fp8)
         return paged ? launch_kernel(mfa_attn_split_kernel<true, true>, grid, block, l, a)
                      : launch_kernel(mfa_attn_split_kernel<true, false>, grid, block, l, a);

@@ -38,7 +38,15 @@ struct AttnArgs {
     int32_t fuse_max;       // sequences with 2..fuse_max chunks are merged in the attention kernel
     float score_scale;      // softmax_scale * k_scale * log2(e)
     float v_scale;          // 1 for bf16
+    int32_t balanced;       // 1: equal step ranges per workgroup (chunk, n_chunk unused)
+    int32_t batch;          // sequences in the call (balanced mode)
+    int32_t part_stride;    // workspace partial slots per sequence (balanced mode)
 };
+
+// Balanced mode: each workgroup takes at least this many 64-token steps, so
+// that a sequence is cut into at most ceil(steps / 4) + 1 pieces (the
+// workspace holds ceil(max_context / 256) + 1 partial slots per sequence).
+constexpr int kMinBalancedSteps = 4;
 
 // Launches whose sequences all have at most this many chunks merge them
 // inside the attention kernel (the last chunk to finish does it); other
@@ -50,7 +58,7 @@ constexpr int kFusedMaxChunks = 2;
 // attention kernel keeps a chunk's page indices in two registers per lane).
 constexpr int kMaxPagedChunkSteps = 128;
 
-hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int batch, const Launch& l);
+hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l);
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l);
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
                          void* v_dst, const Launch& l);

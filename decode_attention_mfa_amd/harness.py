@@ -47,6 +47,7 @@ class DeviceCase:
     softmax_scale: float = 1.0 / 16.0
     rms_eps: float = 1e-6
     split_tokens: int = 0
+    min_len: int = 0             # lower bound of the lengths (as a scheduler knows it), 0 = unknown
 
     @property
     def paged(self) -> bool:
@@ -55,7 +56,7 @@ class DeviceCase:
     def kv(self, max_seq_len: int = 0):
         return make_kv(self.k, self.v, self.seq_lens, page_table=self.page_table,
                        k_scale=self.k_scale, v_scale=self.v_scale,
-                       max_seq_len=max_seq_len or self.max_len)
+                       max_seq_len=max_seq_len or self.max_len, min_seq_len=self.min_len)
 
 
 def to_device(case, device="cuda") -> DeviceCase:
@@ -67,7 +68,8 @@ def to_device(case, device="cuda") -> DeviceCase:
         v_scale=case.v_scale, x=_dev(case.x, device), w_qa=_dev(case.w_qa, device),
         gamma=_dev(case.gamma, device), w_qb=_dev(case.w_qb, device),
         w_k=_dev(getattr(case, "w_k", None), device), w_v=_dev(getattr(case, "w_v", None), device),
-        softmax_scale=case.softmax_scale, rms_eps=case.rms_eps, split_tokens=case.split_tokens)
+        softmax_scale=case.softmax_scale, rms_eps=case.rms_eps, split_tokens=case.split_tokens,
+        min_len=max(0, int(case.seq_lens.min())) if case.batch else 0)
 
 
 def create_handle(dc: DeviceCase, *, max_batch: Optional[int] = None, max_context: Optional[int] = None,

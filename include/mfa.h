@@ -54,6 +54,13 @@ enum mfa_kv_dtype {
 
 typedef struct mfa_ctx* mfa_handle;
 
+/* mfa_config.split_tokens value: cut the work of each call into equal ranges
+ * of 64-token steps, one range per workgroup, over all sequences in order
+ * (the work-centric decomposition of Stream-K, cited by title on the
+ * DeepSeek-V4 references), whatever the lengths. A sequence cut into several
+ * pieces is merged by the last piece to finish, in piece order. */
+#define MFA_SPLIT_BALANCED (-1)
+
 /* Layer configuration (host struct, copied by mfa_create). */
 typedef struct {
     int32_t hidden;        /* model width, 7168; multiple of 512 */
@@ -64,8 +71,10 @@ typedef struct {
     int32_t page_size;     /* 0 = contiguous cache; otherwise must be 64 */
     int32_t max_batch;     /* largest batch any call will pass, >= 1 */
     int32_t max_context;   /* largest sequence length any call will pass, >= 1 */
-    int32_t split_tokens;  /* split-K chunk in tokens, multiple of 64; 0 = chosen per call;
-                              at most 8192 with a paged cache (else MFA_ERR_UNSUPPORTED) */
+    int32_t split_tokens;  /* split-K chunk in tokens, multiple of 64, at most 8192 with a
+                              paged cache (else MFA_ERR_UNSUPPORTED); MFA_SPLIT_BALANCED;
+                              or 0 = chosen per call (balanced when batch >= CUs / 2,
+                              else chunks sized for the batch) */
     float rms_eps;         /* RMSNorm epsilon (1e-6), >= 0 */
     float softmax_scale;   /* score scale (1/16 = 1/sqrt(256)), finite and > 0 */
 } mfa_config;
@@ -92,13 +101,16 @@ typedef struct {
     int64_t kv_stride;          /* contiguous: token slots per sequence, >= max_seq_len */
     int32_t max_seq_len;        /* (host) upper bound of seq_lens in this call, sizes the
                                    launch; 0 = the handle's max_context */
+    int32_t min_seq_len;        /* (host) lower bound of seq_lens in this call, or 0 if
+                                   unknown. Steers only the choice of work split (a
+                                   wrong bound costs time, never correctness) */
 } mfa_kv;
 
 /* Create a handle for one layer shape. Validates `cfg` (host pointer) and
  * allocates the split-K workspace on the current device:
- *   max_batch * ceil(max_context / C) * 64 * (256 + 1) * 4 bytes of chunk
- *   partials, C = split_tokens or, when that is 0, 256 (the smallest chunk
- *   chosen per call), max_batch 4-byte arrival counters (zeroed here, left
+ *   max_batch * (ceil(max_context / C) + 1) * 64 * (256 + 1) * 4 bytes of
+ *   chunk partials, C = split_tokens when positive, else 256 (the smallest
+ *   piece a per-call choice or a balanced split makes), max_batch 4-byte arrival counters (zeroed here, left
  *   at zero by every call), Q-projection scratch of
  *   max_batch * q_rank * (4 * hidden / 512 + 2) bytes, and K/V-projection
  *   partials of 2 * (hidden / 256) * max_batch * 256 * 4 bytes.
@@ -125,14 +137,17 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
  * q [batch][64][256] bf16; out [batch][64][256] bf16; lse_out [batch][64]
  * fp32 or NULL. L_b = 0 gives out = 0 and lse = -inf.
  * The KV range of each sequence is cut into chunks of split_tokens tokens
- * (or a per-call choice when split_tokens is 0); chunk partials go to the
- * handle's workspace and are merged by the log-sum-exp identity, in chunk
- * order: inside the attention kernel by the last chunk to finish when no
- * sequence of the call has more than two chunks, else by a second kernel on
- * the same stream. The result
- * depends only on the logical K/V values and the chunking, not on the cache
- * layout: paged and contiguous caches holding the same rows give bitwise
- * equal outputs. 1 <= batch <= max_batch. */
+ * (or a per-call choice when split_tokens is 0), or by a balanced split
+ * (MFA_SPLIT_BALANCED, and the per-call choice for batches of at least half
+ * the CU count whose length bounds do not show equal step counts) into the
+ * pieces that equal ranges of steps over the whole batch give; partials go to
+ * the handle's workspace and are merged by the log-sum-exp identity, in
+ * chunk order: inside the attention kernel by the last chunk to finish when
+ * no sequence of the call has more than two chunks or the split is balanced,
+ * else by a second kernel on the same stream. The result depends only on the
+ * logical K/V values, the lengths and the chunking, not on the cache layout:
+ * paged and contiguous caches holding the same rows give bitwise equal
+ * outputs. 1 <= batch <= max_batch. */
 int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out,
                int32_t batch, void* hip_stream);
 
@@ -155,8 +170,10 @@ int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* 
 int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v,
                   const mfa_kv* kv, int32_t batch, void* hip_stream);
 
-/* The split-K chunk (tokens) mfa_decode uses for this batch and kv->max_seq_len. */
-int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len);
+/* The split-K chunk (tokens) mfa_decode uses for this batch and the length
+ * bounds kv->max_seq_len and kv->min_seq_len; 0 when it uses the balanced
+ * split. */
+int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len);
 
 /* Test support: copy the logical K and V rows t < L_b of sequence b into
  * contiguous device buffers k_dst, v_dst ([max_seq_len][256] elements of the

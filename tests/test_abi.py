@@ -44,6 +44,7 @@ def _create(**kw):
     (dict(kv_dtype=7), -1, "kv_dtype"),
     (dict(max_batch=0), -1, "max_batch"),
     (dict(split_tokens=100), -1, "split_tokens"),
+    (dict(split_tokens=-2), -1, "split_tokens"),
     (dict(page_size=64, split_tokens=8256), -2, "paged cache"),
     (dict(softmax_scale=0.0), -1, "softmax_scale"),
     (dict(softmax_scale=float("inf")), -1, "softmax_scale"),

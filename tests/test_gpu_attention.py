@@ -95,6 +95,51 @@ def test_paged_ragged_reduced():
                  label="paged ragged B=24 split=128")
 
 
+BAL = -1   # MFA_SPLIT_BALANCED
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("paged", [False, True])
+def test_balanced_ragged(kv, paged):
+    """Equal step ranges per workgroup over ragged lengths (empty, one token,
+    page edges): pieces that start and end inside sequences."""
+    L = [0, 1, 63, 64, 65, 127, 129, 1000, 2049, 0, 300]
+    case = synth.make_case("bal", len(L), L, kv, seed=81, paged=paged, kv_slack=0 if paged else 5)
+    check_parity(case, split_tokens=BAL, label=f"balanced ragged {kv} paged={paged}")
+
+
+def test_balanced_many_short_sequences():
+    """Several sequences per workgroup range (300 sequences of 0..299 tokens)."""
+    L = np.random.default_rng(82).integers(0, 300, 300).astype(np.int32)
+    case = synth.make_case("bal_short", len(L), L, "fp8", seed=83, paged=True)
+    check_parity(case, split_tokens=BAL, label="balanced 300 short sequences fp8 paged")
+
+
+def test_balanced_long_and_short():
+    """One long sequence among short ones is cut into ~80 pieces, merged by
+    the last piece to finish."""
+    case = synth.make_case("bal_long", 4, [20000, 10, 5, 3000], "bf16", seed=84)
+    check_parity(case, split_tokens=BAL, label="balanced long + short bf16")
+
+
+def test_balanced_auto_for_large_batches():
+    """The per-call choice takes the balanced split for a batch of 128 or
+    more (fp8 paged ragged, reduced lengths)."""
+    m, hz = _mfa()
+    case = synth.config_case(4, batch=160, scale_len=1 / 32)
+    dc = hz.to_device(case)
+    h = hz.create_handle(dc, split_tokens=0)
+    try:
+        # lengths unknown, or known to differ in step count: balanced
+        assert m.mfa_split_tokens(h, dc.batch, dc.max_len) == 0
+        assert m.mfa_split_tokens(h, dc.batch, dc.max_len, dc.min_len) == 0
+        # every sequence with the same number of steps: equal chunks
+        assert m.mfa_split_tokens(h, dc.batch, 4096, 4033) > 0
+    finally:
+        m.mfa_destroy(h)
+    check_parity(case, split_tokens=0, label="paged ragged B=160 auto (balanced)")
+
+
 def test_long_splitk_reduced():
     check_parity(synth.config_case(5, batch=4, scale_len=1 / 16), label="long split-K B=4 L=2K/4K")
 
@@ -116,7 +161,7 @@ def test_paged_equals_contiguous_bitwise():
             vc[b, :len(t)] = pc.v[pages, t % 64]
         cc = synth.Case(name="c", batch=pc.batch, kv_dtype=kv, seq_lens=pc.seq_lens, k=kc, v=vc,
                         q=pc.q, k_scale=pc.k_scale, v_scale=pc.v_scale)
-        for split in (128, 512):
+        for split in (128, 512, BAL):
             _say(f"[bitwise] paged vs contiguous {kv} split={split}")
             o1, l1, _ = hz.run_case(hz.to_device(pc), split_tokens=split)
             o2, l2, _ = hz.run_case(hz.to_device(cc), split_tokens=split)
@@ -150,9 +195,10 @@ def test_deterministic_run_twice():
     case = synth.config_case(4, batch=16, scale_len=1 / 16)
     dc = hz.to_device(case)
     _say("[determinism] paged fp8 B=16, two runs")
-    o1, l1, _ = hz.run_case(dc, split_tokens=128)
-    o2, l2, _ = hz.run_case(dc, split_tokens=128)
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for split in (128, BAL):
+        o1, l1, _ = hz.run_case(dc, split_tokens=split)
+        o2, l2, _ = hz.run_case(dc, split_tokens=split)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_lse_null_is_allowed():
@@ -225,12 +271,13 @@ def test_dominant_late_keys_restart(kv):
         check_parity(case, split_tokens=split, label=f"dominant late keys {kv} split={split}")
 
 
-@pytest.mark.parametrize("split", [1024, 256])
+@pytest.mark.parametrize("split", [1024, 256, -1])
 def test_graph_replay_matches_eager(split):
     """mfa_decode captured into a HIP graph (through torch's capture on a side
     stream), replayed several times with other eager decodes in between: every
     replay equals the eager result bitwise. split 1024 merges the two chunks in
-    the attention kernel, 256 uses the combine kernel."""
+    the attention kernel, 256 uses the combine kernel, -1 (balanced) merges
+    the pieces in the attention kernel."""
     m, hz = _mfa()
     case = synth.config_case(3, batch=3, scale_len=0.5)
     other = synth.config_case(3, batch=3, scale_len=0.5, q_std=2.0)
