@@ -39,8 +39,9 @@ sys.path.insert(0, ROOT)
 METRIC = "MFA decode tokens/s per layer (1 GPU) + achieved HBM GB/s vs roofline"
 HBM_PEAK_GBPS = 8000.0
 WORKLOADS = {"tiny": 1, "full_layer": 2, "fp8_contig": 3, "paged_ragged": 4, "long_splitk": 5,
-             "decode_step": 2, "paged_append": 4}
+             "decode_step": 2, "paged_append": 4, "fp8_mtp2": 3, "fp8_mtp4": 3}
 APPEND = ("decode_step", "paged_append")
+MTP = {"fp8_mtp2": 2, "fp8_mtp4": 4}   # query tokens per sequence
 DESCRIPTION = {
     "tiny": "B=1, L=256, bf16 KV, contiguous, decode only",
     "full_layer": "B=32, L=4096, bf16 KV, contiguous, Q projection 7168->2048 (RMSNorm)->64x256 + decode",
@@ -51,6 +52,8 @@ DESCRIPTION = {
                    "+ decode over L_b+1",
     "paged_append": "B=384, L~U[1024,8192], FP8-E4M3 KV, 64-token pages: KV append (7168->256 x2, E4M3, "
                     "row L_b) + decode over L_b+1",
+    "fp8_mtp2": "B=128, L=4096, FP8-E4M3 KV, contiguous, 2 query tokens per sequence (multi-token decode)",
+    "fp8_mtp4": "B=128, L=4096, FP8-E4M3 KV, contiguous, 4 query tokens per sequence (multi-token decode)",
 }
 # sources that decide the attention kernel's memory traffic (kernel, launch
 # shape, split and merge policy); the stored HBM counters hold for this hash
@@ -73,7 +76,7 @@ def attn_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(case, attention_writes_out: bool, append: bool = False):
+def algorithmic_bytes(case, attention_writes_out: bool, append: bool = False, qtok: int = 1):
     """(attention-kernel bytes, whole-step bytes) the method must move.
     Attention: every cached K and V row t < L_b (512 B per token with FP8,
     1024 B with bf16; t <= L_b after an append), Q (32 KB per sequence), the
@@ -88,8 +91,8 @@ def algorithmic_bytes(case, attention_writes_out: bool, append: bool = False):
     L = case.seq_lens.astype(np.int64) + (1 if append else 0)
     elem = 1 if case.kv_dtype == "fp8" else 2
     kv = int(L.sum()) * 2 * 256 * elem
-    q = B * 64 * 256 * 2
-    o = B * 64 * 256 * 2
+    q = B * qtok * 64 * 256 * 2
+    o = B * qtok * 64 * 256 * 2
     meta = B * 4
     if case.paged:
         meta += int(((L + 63) // 64).sum()) * 4
@@ -137,10 +140,17 @@ def cpu_baseline(case, budget_s: float):
     a one-sequence probe so that the run takes about budget_s seconds."""
     import oracle
 
+    qtok = case.q.shape[1] if case.q is not None and case.q.ndim == 4 else 1
+
     def work(s):
         if s.w_k is not None:
             oracle.kv_project(s.x, s.w_k, s.w_v)
-        oracle.case_attention(s)
+        if qtok > 1:
+            oracle.attention_mtp(oracle.decode_bf16(s.q), s.k, s.v, s.seq_lens,
+                                 kv_dtype=oracle.KV_FP8 if s.kv_dtype == "fp8" else oracle.KV_BF16,
+                                 k_scale=s.k_scale, v_scale=s.v_scale, page_table=s.page_table)
+        else:
+            oracle.case_attention(s)
 
     t0 = time.perf_counter()
     work(sample_case(case, 1))
@@ -152,7 +162,7 @@ def cpu_baseline(case, budget_s: float):
     dt = time.perf_counter() - t0
     what = " + ".join(w for w, on in (("Q projection", case.w_qa is not None),
                                        ("K/V projection", case.w_k is not None), ("attention", True)) if on)
-    return {"value": n / dt, "unit": "tokens/s/layer", "cores": oracle.max_threads(), "kind": "oracle",
+    return {"value": n * qtok / dt, "unit": "tokens/s/layer", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"{what} of the first {n} of {case.batch} sequences, fp64, {dt:.1f} s"}
 
 
@@ -208,9 +218,12 @@ def main():
     log(f"[bench] generating workload {wl}: {DESCRIPTION[wl]}")
     t0 = time.perf_counter()
     append = wl in APPEND
+    qtok = MTP.get(wl, 1)
     case = synth.config_case(WORKLOADS[wl], append=append)
+    if qtok > 1:
+        case.q = synth.mtp_queries(case.batch, qtok, case.seed)
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s")
-    _, step_bytes = algorithmic_bytes(case, True, append)
+    _, step_bytes = algorithmic_bytes(case, True, append, qtok)
 
     dc = harness.to_device(case)
     # rotate copies of the per-step inputs so that no step finds them in the MALL
@@ -236,10 +249,15 @@ def main():
     attn_lens = dc.seq_lens + 1 if append else dc.seq_lens
     attn_max = dc.max_len + 1 if append else dc.max_len
     attn_min = dc.min_len + 1 if append else dc.min_len
-    h = harness.create_handle(dc, split_tokens=args.split, max_context=attn_max)
-    split = mfa.mfa_split_tokens(h, dc.batch, attn_max, attn_min)
+    h = harness.create_handle(dc, split_tokens=args.split, max_context=attn_max, max_batch=dc.batch * qtok)
+    # multi-token decode uses the chunked split, sized for batch x tokens rows
+    split = mfa.mfa_split_tokens(h, dc.batch * qtok, attn_max, attn_max if qtok > 1 else attn_min)
     stream = torch.cuda.Stream()
-    outs = [harness.alloc_outputs(dc) for _ in range(nrot)]
+    if qtok > 1:
+        outs = [(torch.empty((dc.batch, qtok, 64, 256), dtype=torch.int16, device="cuda"),
+                 torch.empty((dc.batch, qtok, 64), dtype=torch.float32, device="cuda")) for _ in range(nrot)]
+    else:
+        outs = [harness.alloc_outputs(dc) for _ in range(nrot)]
     qbufs = [torch.empty((dc.batch, 64, 256), dtype=torch.int16, device="cuda") for _ in range(nrot)]
 
     kvs = [c.kv() for c in sets]
@@ -256,7 +274,10 @@ def main():
         if append:
             # writes row L_b (the same row every step: the cache stays as it is)
             mfa.mfa_kv_append(h, s.x, s.w_k, s.w_v, kvs[i % nrot], s.batch, stream)
-        mfa.mfa_decode(h, q, attn_kvs[i % nrot], o, l, s.batch, stream)
+        if qtok > 1:
+            mfa.mfa_decode_mtp(h, q, attn_kvs[i % nrot], qtok, o, l, s.batch, stream)
+        else:
+            mfa.mfa_decode(h, q, attn_kvs[i % nrot], o, l, s.batch, stream)
 
     def run(n):
         torch.cuda.synchronize()
@@ -287,8 +308,8 @@ def main():
     args.warmup = warmup
 
     ms_per_step = dt * 1e3 / args.steps
-    value = dc.batch / (ms_per_step / 1e3)
-    attn_bytes, _ = algorithmic_bytes(case, prof["combine"][0] == 0, append)
+    value = dc.batch * qtok / (ms_per_step / 1e3)
+    attn_bytes, _ = algorithmic_bytes(case, prof["combine"][0] == 0, append, qtok)
     n_attn, ms_attn = prof["attention"]
     attn_ms = ms_attn / max(n_attn, 1)
     achieved = attn_bytes / (attn_ms / 1e3) / 1e9
@@ -306,6 +327,7 @@ def main():
                    "context_min": int(case.seq_lens.min()), "context_max": int(case.seq_lens.max()),
                    "kv_dtype": "fp8_e4m3" if case.kv_dtype == "fp8" else "bf16",
                    "layout": "paged64" if case.paged else "contiguous", "split_tokens": split,
+                   "query_tokens": qtok,
                    "work_split": "balanced ranges of steps" if split == 0 else f"chunks of {split} tokens",
                    "input_sets_rotated": nrot, "mall": "cold" if cold else "warm"},
         "step_hbm_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),

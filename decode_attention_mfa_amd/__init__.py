@@ -63,6 +63,8 @@ def _load_lib():
     lib.mfa_qproj.argtypes = [P, P, P, P, P, P, I32, P]
     lib.mfa_qproj.restype = ctypes.c_int
     lib.mfa_decode.argtypes = [P, P, ctypes.POINTER(mfa_kv), P, P, I32, P]
+    lib.mfa_decode_mtp.argtypes = [P, P, ctypes.POINTER(mfa_kv), I32, P, P, I32, P]
+    lib.mfa_decode_mtp.restype = ctypes.c_int
     lib.mfa_kv_append.argtypes = [P, P, P, P, ctypes.POINTER(mfa_kv), I32, P]
     lib.mfa_kv_append.restype = ctypes.c_int
     lib.mfa_decode.restype = ctypes.c_int
@@ -159,6 +161,12 @@ def mfa_qproj(h: int, x, w_qa, rms_w, w_qb, q_out, batch: int, stream=None) -> N
 def mfa_decode(h: int, q, kv: mfa_kv, out, lse_out, batch: int, stream=None) -> None:
     _check(lib.mfa_decode(h, _ptr(q), ctypes.byref(kv), _ptr(out), _ptr(lse_out), batch,
                           _stream(stream)), "mfa_decode")
+
+
+def mfa_decode_mtp(h: int, q, kv: mfa_kv, num_tokens: int, out, lse_out, batch: int, stream=None) -> None:
+    """num_tokens query tokens per sequence: q, out [batch, num_tokens, 64, 256]."""
+    _check(lib.mfa_decode_mtp(h, _ptr(q), ctypes.byref(kv), num_tokens, _ptr(out), _ptr(lse_out), batch,
+                              _stream(stream)), "mfa_decode_mtp")
 
 
 def mfa_kv_append(h: int, x, w_k, w_v, kv: mfa_kv, batch: int, stream=None) -> None:

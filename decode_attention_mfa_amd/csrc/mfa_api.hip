@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <new>
+#include <string>
 #include <vector>
 
 #include "mfa.h"
@@ -322,14 +323,20 @@ static mfa::KvView make_view(const mfa_ctx* h, const mfa_kv* kv, int32_t max_len
     return v;
 }
 
-int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out, int32_t batch,
-               void* hip_stream) {
-    g_last_error[0] = 0;
-    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_decode: not a live handle");
-    if (!q || !out) return fail(MFA_ERR_INVALID, "mfa_decode: null q or out");
+// mfa_decode (qtok 1) and mfa_decode_mtp (qtok query tokens per sequence).
+static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok, void* out, float* lse_out,
+                       int32_t batch, void* hip_stream, const char* fn) {
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "%s: not a live handle", fn);
+    if (!q || !out) return fail(MFA_ERR_INVALID, "%s: null q or out", fn);
+    if (qtok < 1 || qtok > mfa::kMaxQueryTokens)
+        return fail(MFA_ERR_INVALID, "%s: num_tokens %d outside [1, %d]", fn, qtok, mfa::kMaxQueryTokens);
     int32_t max_len = 0;
-    int rc = check_kv(h, kv, batch, "mfa_decode", &max_len);
+    int rc = check_kv(h, kv, batch, fn, &max_len);
     if (rc) return rc;
+    const int32_t rows = batch * qtok;   // query-row sets (one per sequence and token)
+    if (rows > h->cfg.max_batch)
+        return fail(MFA_ERR_INVALID, "%s: batch %d x num_tokens %d exceeds max_batch %d", fn, batch, qtok,
+                    h->cfg.max_batch);
     const bool fp8 = h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3;
     mfa::AttnArgs a;
     a.q = (const uint16_t*)q;
@@ -340,8 +347,9 @@ int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* 
     a.part_lse = h->part_lse;
     a.counters = h->counters;
     a.batch = batch;
+    a.qtok = qtok;
     int workgroups;
-    if (use_balanced(h, batch, max_len, kv->min_seq_len)) {
+    if (qtok == 1 && use_balanced(h, batch, max_len, kv->min_seq_len)) {
         // equal ranges of at least 4 and at most 128 steps: one workgroup per
         // CU, or more when the batch's steps could exceed 128 per workgroup
         a.balanced = 1;
@@ -355,14 +363,15 @@ int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* 
         workgroups = (int)g;
     } else {
         a.balanced = 0;
-        a.chunk = choose_split(h, batch, max_len);
+        a.chunk = choose_split(h, rows, max_len);
         a.n_chunk = (max_len + a.chunk - 1) / a.chunk;
         if (a.n_chunk < 1) a.n_chunk = 1;
         if (a.n_chunk > h->max_chunks)
-            return fail(MFA_ERR_INVALID, "mfa_decode: %d chunks exceed the workspace (%d)", a.n_chunk, h->max_chunks);
+            return fail(MFA_ERR_INVALID, "%s: %d chunks exceed the workspace (%d)", fn, a.n_chunk, h->max_chunks);
         a.part_stride = a.n_chunk;
         a.fuse_max = a.n_chunk <= mfa::kFusedMaxChunks ? mfa::kFusedMaxChunks : 1;
-        workgroups = batch * a.n_chunk;
+        // multi-token: groups of 8 work items times qtok tokens (see the kernel)
+        workgroups = qtok == 1 ? batch * a.n_chunk : round_up((int64_t)batch * a.n_chunk, 8) * qtok;
     }
     const float log2e = 1.4426950408889634f;
     a.score_scale = h->cfg.softmax_scale * (fp8 ? kv->k_scale : 1.0f) * log2e;
@@ -372,9 +381,21 @@ int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* 
     hipError_t e = timed_launch(h, MFA_KERNEL_ATTENTION, st,
                                 [&](const mfa::Launch& l) { return mfa::launch_attn_split(a, fp8, paged, workgroups, l); });
     if (e == hipSuccess && !a.balanced && a.n_chunk > a.fuse_max)
-        e = timed_launch(h, MFA_KERNEL_COMBINE, st, [&](const mfa::Launch& l) { return mfa::launch_combine(a, batch, l); });
-    if (e != hipSuccess) return hip_fail(e, "mfa_decode: launch");
+        e = timed_launch(h, MFA_KERNEL_COMBINE, st, [&](const mfa::Launch& l) { return mfa::launch_combine(a, rows, l); });
+    if (e != hipSuccess) return hip_fail(e, (std::string(fn) + ": launch").c_str());
     return MFA_OK;
+}
+
+int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out, int32_t batch,
+               void* hip_stream) {
+    g_last_error[0] = 0;
+    return decode_impl(h, q, kv, 1, out, lse_out, batch, hip_stream, "mfa_decode");
+}
+
+int mfa_decode_mtp(mfa_handle h, const void* q, const mfa_kv* kv, int32_t num_tokens, void* out, float* lse_out,
+                   int32_t batch, void* hip_stream) {
+    g_last_error[0] = 0;
+    return decode_impl(h, q, kv, num_tokens, out, lse_out, batch, hip_stream, "mfa_decode_mtp");
 }
 
 int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v, const mfa_kv* kv,

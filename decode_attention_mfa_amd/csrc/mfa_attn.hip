@@ -144,17 +144,40 @@ __device__ __forceinline__ void wait_vmem() {
 //            attend_piece, and the last of a sequence's pieces to finish
 //            merges them.
 // Both run the same piece body (the two .inc files).
+//
+// Multi-token decode (MTP, chunked kernel only): each cache sequence kvb has
+// t = p.qtok query tokens, query rows b = kvb*t + j; token j attends to the
+// first L_kvb - (t-1-j) rows (the cache already holds the t new tokens, the
+// last at row L - 1). The t workgroups of one (sequence, chunk) get block
+// indices 8 apart inside a group of 8t, so that the round-robin dispatch puts
+// them on one XCD at about the same time: the KV bytes come from HBM once and
+// from that XCD's L2 for the other tokens.
 
-template <bool FP8, bool PAGED>
+template <bool FP8, bool PAGED, bool MTP>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mfa_attn_split_kernel(const AttnArgs p) {
 #define MFA_PIECE_TID threadIdx.x
 #include "mfa_attn_piece_setup.inc"
 #undef MFA_PIECE_TID
 
-    const int b = blockIdx.x / p.n_chunk;
-    const int c = blockIdx.x - b * p.n_chunk;
-    const int L = seq_len(p.kv, b);
+    int b, c, kvb, L;
+    if constexpr (!MTP) {
+        b = blockIdx.x / p.n_chunk;
+        c = blockIdx.x - b * p.n_chunk;
+        kvb = b;
+        L = seq_len(p.kv, b);
+    } else {
+        const int t = p.qtok;
+        const int grp = blockIdx.x / (8 * t);
+        const int r = blockIdx.x - grp * 8 * t;
+        const int wi = grp * 8 + (r & 7);   // (sequence, chunk) work item
+        if (wi >= p.batch * p.n_chunk) return;
+        kvb = wi / p.n_chunk;
+        c = wi - kvb * p.n_chunk;
+        const int j = r >> 3;
+        b = kvb * t + j;
+        L = max(0, seq_len(p.kv, kvb) - (t - 1 - j));
+    }
     const int t_begin = c * p.chunk;
 
     if (t_begin >= L) {
@@ -201,6 +224,7 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& p, const int b, con
 #include "mfa_attn_piece_setup.inc"
 #undef MFA_PIECE_TID
 
+    const int kvb = b;
     const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
     const int last_s = nsteps - 1;
     const bool single = nparts == 1;
@@ -341,7 +365,8 @@ __global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
     const int b = blockIdx.x >> 6;
     const int h = blockIdx.x & 63;
     const int t = threadIdx.x;
-    const int L = seq_len(p.kv, b);
+    // multi-token decode: query row b is token b % qtok of cache sequence b / qtok
+    const int L = p.qtok > 1 ? max(0, seq_len(p.kv, b / p.qtok) - (p.qtok - 1 - b % p.qtok)) : seq_len(p.kv, b);
     const int nc = (L + p.chunk - 1) / p.chunk;
     if (nc <= p.fuse_max) return;   // merged by the attention kernel itself
     const int64_t base = (int64_t)b * p.n_chunk;
@@ -414,11 +439,18 @@ hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgr
         return paged ? launch_kernel(mfa_attn_balanced_kernel<false, true>, grid, block, l, a)
                      : launch_kernel(mfa_attn_balanced_kernel<false, false>, grid, block, l, a);
     }
+    if (a.qtok > 1) {
+        if (fp8)
+            return paged ? launch_kernel(mfa_attn_split_kernel<true, true, true>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_split_kernel<true, false, true>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_split_kernel<false, true, true>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_split_kernel<false, false, true>, grid, block, l, a);
+    }
     if (fp8)
-        return paged ? launch_kernel(mfa_attn_split_kernel<true, true>, grid, block, l, a)
-                     : launch_kernel(mfa_attn_split_kernel<true, false>, grid, block, l, a);
-    return paged ? launch_kernel(mfa_attn_split_kernel<false, true>, grid, block, l, a)
-                 : launch_kernel(mfa_attn_split_kernel<false, false>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_split_kernel<true, true, false>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_split_kernel<true, false, false>, grid, block, l, a);
+    return paged ? launch_kernel(mfa_attn_split_kernel<false, true, false>, grid, block, l, a)
+                 : launch_kernel(mfa_attn_split_kernel<false, false, false>, grid, block, l, a);
 }
 
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l) {

@@ -39,7 +39,8 @@ struct AttnArgs {
     float score_scale;      // softmax_scale * k_scale * log2(e)
     float v_scale;          // 1 for bf16
     int32_t balanced;       // 1: equal step ranges per workgroup (chunk, n_chunk unused)
-    int32_t batch;          // sequences in the call (balanced mode)
+    int32_t batch;          // cache sequences in the call (balanced and multi-token modes)
+    int32_t qtok;           // query tokens per sequence (1, or t for multi-token decode)
     int32_t part_stride;    // workspace partial slots per sequence (balanced mode)
 };
 
@@ -47,6 +48,9 @@ struct AttnArgs {
 // that a sequence is cut into at most ceil(steps / 4) + 1 pieces (the
 // workspace holds ceil(max_context / 256) + 1 partial slots per sequence).
 constexpr int kMinBalancedSteps = 4;
+
+// Multi-token decode: at most this many query tokens per sequence.
+constexpr int kMaxQueryTokens = 16;
 
 // Launches whose sequences all have at most this many chunks merge them
 // inside the attention kernel (the last chunk to finish does it); other

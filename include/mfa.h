@@ -151,6 +151,24 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
 int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out,
                int32_t batch, void* hip_stream);
 
+/* Multi-token decode (several new tokens per sequence in one step, as
+ * multi-token prediction does; Step-3 Key points name it among the future
+ * directions): num_tokens query tokens per sequence attend to the same cache.
+ * The cache already holds the new tokens' K/V rows, token j of sequence b at
+ * row L_b - num_tokens + j, and token j sees rows t < L_b - (num_tokens-1-j)
+ * (itself and everything before it; a token with no row gives out = 0, lse =
+ * -inf):
+ *   q [batch][num_tokens][64][256] bf16, out [batch][num_tokens][64][256]
+ *   bf16, lse_out [batch][num_tokens][64] fp32 or NULL.
+ * Each cached row is fetched from HBM once for all num_tokens tokens (their
+ * workgroups run side by side on one XCD and share its L2). Uses the chunked
+ * split (split_tokens, or the per-call choice for batch * num_tokens rows).
+ * 1 <= num_tokens <= 16; batch * num_tokens <= max_batch (the workspace holds
+ * partials per query token). num_tokens = 1 is mfa_decode with the chunked
+ * split. */
+int mfa_decode_mtp(mfa_handle h, const void* q, const mfa_kv* kv, int32_t num_tokens, void* out,
+                   float* lse_out, int32_t batch, void* hip_stream);
+
 /* KV append: the new token's key and value rows, written into the cache
  * before that token's attention (Step-3 Key points: one shared key head and
  * one shared value head of 256, so one K row and one V row per token; the

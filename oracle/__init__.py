@@ -221,6 +221,30 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, *, kv_dtype
     return o, lse
 
 
+def attention_mtp(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, *, kv_dtype: int,
+                  k_scale: float = 1.0, v_scale: float = 1.0, page_table=None, page_size: int = 64,
+                  softmax_scale: float = 1.0 / 16.0, nthreads: int = 0):
+    """Multi-token decode: q [B, t, H, D] fp64, the cache holding the t new
+    tokens as its last rows; token j of sequence b attends to the rows
+    s < L_b - (t-1-j) (itself and all before it). Returns (o [B, t, H, D],
+    lse [B, t, H]). Each (sequence, token) is one call of ``attention``."""
+    q = _c(q, np.float64)
+    B, t, H, D = q.shape
+    L = _c(seq_lens, np.int32)
+    Lv = np.maximum(0, np.repeat(L, t) - np.tile(np.arange(t - 1, -1, -1), B)).astype(np.int32)
+    if page_table is not None:
+        pt = np.repeat(_c(page_table, np.int32), t, axis=0)
+        kk, vv = k, v
+    else:
+        pt = None
+        kk = np.repeat(np.ascontiguousarray(k), t, axis=0)
+        vv = np.repeat(np.ascontiguousarray(v), t, axis=0)
+    o, lse = attention(q.reshape(B * t, H, D), kk, vv, Lv, kv_dtype=kv_dtype, k_scale=k_scale,
+                       v_scale=v_scale, page_table=pt, page_size=page_size, softmax_scale=softmax_scale,
+                       nthreads=nthreads)
+    return o.reshape(B, t, H, D), lse.reshape(B, t, H)
+
+
 def weights(q: np.ndarray, k: np.ndarray, seq_lens, b: int, h: int, *, kv_dtype: int,
             k_scale: float = 1.0, page_table=None, softmax_scale: float = 1.0 / 16.0):
     """Softmax weights of head h of sequence b over its L_b tokens."""

@@ -243,3 +243,11 @@ def _with_append(base: Case) -> Case:
     if base.q is not None:
         c.q = base.q
     return c
+
+
+def mtp_queries(batch: int, t: int, seed: int) -> np.ndarray:
+    """Queries of multi-token decode: bf16 bits [batch, t, 64, 256], N(0,1),
+    from the "q" stream of ``seed``'s streams (t = 1 gives the single-token Q
+    of a case built with the same seed)."""
+    g = _streams(seed)["q"]
+    return bf16_bits(_normal(g, (batch, t, NUM_HEADS, HEAD_DIM)))

@@ -503,3 +503,38 @@ def test_kv_append_paged_matches_contiguous(kv):
     owned = np.unique(case.page_table[case.page_table >= 0])
     free = np.setdiff1d(np.arange(case.k.shape[0]), owned)
     assert np.array_equal(kp[free], case.k[free]) and np.array_equal(vp[free], case.v[free])
+
+
+# ------------------------------------------------------------------ multi-token decode
+
+def test_mtp_matches_torch_sdpa_with_causal_mask():
+    """t query tokens per sequence, the last t cache rows being theirs: against
+    torch's scaled_dot_product_attention with an explicit boolean mask
+    (query j may see keys s < L - (t-1-j)), K and V broadcast to the heads."""
+    t, H, D = 3, 64, 256
+    for L in (3, 10, 70):
+        case = synth.make_case("mtp", 1, L, "bf16", seed=90 + L)
+        rng = np.random.default_rng(91)
+        q = _torch_decode_bf16(synth.bf16_bits(rng.standard_normal((1, t, H, D)).astype(np.float32)))
+        o, lse = oracle.attention_mtp(q, case.k, case.v, case.seq_lens, kv_dtype=BF16)
+        K, V = _kv_decoded(case)
+        Kt = torch.from_numpy(K[0, :L]).to(torch.float64)
+        Vt = torch.from_numpy(V[0, :L]).to(torch.float64)
+        qt = torch.from_numpy(q[0]).permute(1, 0, 2)                     # [H, t, D]
+        mask = torch.arange(L)[None, :] < (L - (t - 1) + torch.arange(t))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, Kt[None].expand(H, L, D), Vt[None].expand(H, L, D), attn_mask=mask, scale=1.0 / 16.0)
+        assert _rel(o[0], ref.permute(1, 0, 2).numpy()) < 1e-12
+        s = torch.einsum("htd,ld->htl", qt, Kt) / 16.0
+        lse_ref = torch.logsumexp(s.masked_fill(~mask[None], float("-inf")), dim=-1).permute(1, 0).numpy()
+        assert np.abs(lse[0] - lse_ref).max() < 1e-12
+
+
+def test_mtp_token_with_no_rows():
+    """A sequence shorter than t: its first tokens see no row (out 0, lse -inf)."""
+    case = synth.make_case("mtp0", 1, 2, "fp8", seed=95)
+    q = np.random.default_rng(96).standard_normal((1, 4, 64, 256))
+    o, lse = oracle.attention_mtp(q, case.k, case.v, case.seq_lens, kv_dtype=FP8, k_scale=case.k_scale,
+                                  v_scale=case.v_scale)
+    assert np.all(o[0, :2] == 0) and np.all(np.isneginf(lse[0, :2]))
+    assert np.all(np.isfinite(lse[0, 2:]))
