@@ -57,7 +57,9 @@ struct mfa_ctx {
     float* part_lse;       // [max_batch * max_chunks][64]
     int32_t* counters;     // [max_batch], zero between calls
     float* c_part;         // [hidden / kQprojRowsPerSplit][max_batch][q_rank]
-    uint16_t* chat;        // [max_batch][q_rank]
+    uint16_t* chat;        // [max_batch][q_rank]: c * gamma, bf16
+    float* sumsq;          // [max_batch][q_rank / 64]
+    int32_t* qcounters;    // [ceil(max_batch / 32)][q_rank / 64], zero between calls
     float* kv_part;        // [2][hidden / kKvRowsPerSplit][max_batch][256]
 };
 
@@ -153,9 +155,9 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     if (c.hidden <= 0 || c.hidden % mfa::kQprojRowsPerSplit != 0)
         return fail(MFA_ERR_UNSUPPORTED, "mfa_create: hidden must be a positive multiple of %d (got %d)",
                     mfa::kQprojRowsPerSplit, c.hidden);
-    if (c.q_rank <= 0 || c.q_rank % 64 != 0 || c.q_rank > 65536)
-        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: q_rank must be a positive multiple of 64 (got %d)",
-                    c.q_rank);
+    if (c.q_rank <= 0 || c.q_rank % 64 != 0 || c.q_rank > 64 * mfa::kMaxNormBlocks)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: q_rank must be a positive multiple of 64, at most %d (got %d)",
+                    64 * mfa::kMaxNormBlocks, c.q_rank);
     if (c.kv_dtype != MFA_DTYPE_BF16 && c.kv_dtype != MFA_DTYPE_FP8_E4M3)
         return fail(MFA_ERR_INVALID, "mfa_create: bad kv_dtype %d", c.kv_dtype);
     if (c.page_size != 0 && c.page_size != mfa::kPage)
@@ -184,6 +186,8 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     const int64_t bytes_c = (int64_t)(c.hidden / mfa::kQprojRowsPerSplit) * c.max_batch * c.q_rank * 4;
     const int64_t bytes_chat = (int64_t)c.max_batch * c.q_rank * 2;
     const int64_t bytes_kv = 2 * (int64_t)(c.hidden / mfa::kKvRowsPerSplit) * c.max_batch * mfa::kHeadDim * 4;
+    const int64_t bytes_sumsq = (int64_t)(c.q_rank / 64) * c.max_batch * 4;
+    const int64_t bytes_qctr = (int64_t)((c.max_batch + 31) / 32) * (c.q_rank / 64) * 4;
     if (max_chunks > (1 << 24) || nparts > (int64_t)1 << 31)
         return fail(MFA_ERR_INVALID, "mfa_create: max_batch * max_context too large");
 
@@ -197,9 +201,10 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
         delete h;
         return hip_fail(e, "mfa_create: device query");
     }
-    constexpr int kBuffers = 6;
-    void* p[kBuffers] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-    const int64_t sizes[kBuffers] = {bytes_o, bytes_lse, bytes_c, bytes_chat, (int64_t)c.max_batch * 4, bytes_kv};
+    constexpr int kBuffers = 8;
+    void* p[kBuffers] = {};
+    const int64_t sizes[kBuffers] = {bytes_o,  bytes_lse, bytes_c,     bytes_chat, (int64_t)c.max_batch * 4,
+                                     bytes_kv, bytes_sumsq, bytes_qctr};
     for (int i = 0; i < kBuffers; i++) {
         e = hipMalloc(&p[i], (size_t)sizes[i]);
         if (e != hipSuccess) {
@@ -216,7 +221,10 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     h->chat = (uint16_t*)p[3];
     h->counters = (int32_t*)p[4];
     h->kv_part = (float*)p[5];
+    h->sumsq = (float*)p[6];
+    h->qcounters = (int32_t*)p[7];
     e = hipMemset(h->counters, 0, (size_t)c.max_batch * 4);
+    if (e == hipSuccess) e = hipMemset(h->qcounters, 0, (size_t)bytes_qctr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         for (int j = 0; j < kBuffers; j++) (void)hipFree(p[j]);
@@ -240,6 +248,8 @@ int mfa_destroy(mfa_handle h) {
     (void)hipFree(h->chat);
     (void)hipFree(h->counters);
     (void)hipFree(h->kv_part);
+    (void)hipFree(h->sumsq);
+    (void)hipFree(h->qcounters);
     delete h;
     return MFA_OK;
 }
@@ -267,15 +277,20 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w, 
     a.q_out = (uint16_t*)q_out;
     a.c_part = h->c_part;
     a.chat = h->chat;
+    a.sumsq = h->sumsq;
+    a.counters = h->qcounters;
     a.batch = batch;
     a.hidden = h->cfg.hidden;
     a.rank = h->cfg.q_rank;
     a.nq = mfa::kHeads * mfa::kHeadDim;
-    a.ksplit = a.hidden / mfa::kQprojRowsPerSplit;
+    // 1024-row K splits when they divide hidden (half the partials the last
+    // split sums), else 512
+    a.ksplit = a.hidden % (2 * mfa::kQprojRowsPerSplit) == 0 ? a.hidden / (2 * mfa::kQprojRowsPerSplit)
+                                                               : a.hidden / mfa::kQprojRowsPerSplit;
     a.eps = h->cfg.rms_eps;
     hipStream_t st = (hipStream_t)hip_stream;
+    // the RMSNorm is split between the two launches (see mfa_qproj.hip)
     hipError_t e = timed_launch(h, MFA_KERNEL_QPROJ_DOWN, st, [&](const mfa::Launch& l) { return mfa::launch_qproj_down(a, l); });
-    if (e == hipSuccess) e = timed_launch(h, MFA_KERNEL_RMSNORM, st, [&](const mfa::Launch& l) { return mfa::launch_rmsnorm(a, l); });
     if (e == hipSuccess) e = timed_launch(h, MFA_KERNEL_QPROJ_UP, st, [&](const mfa::Launch& l) { return mfa::launch_qproj_up(a, l); });
     if (e != hipSuccess) return hip_fail(e, "mfa_qproj: launch");
     return MFA_OK;

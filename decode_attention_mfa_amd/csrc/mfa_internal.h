@@ -74,9 +74,26 @@ struct QprojArgs {
     const uint16_t* w_qb;   // [rank][nq]
     uint16_t* q_out;        // [B][nq]
     float* c_part;          // workspace [ksplit][B][rank] fp32
-    uint16_t* chat;         // workspace [B][rank] bf16
+    uint16_t* chat;         // workspace [B][rank] bf16: c * gamma
+    float* sumsq;           // workspace [B][rank/64]: per row and column block, sum of c^2
+    int32_t* counters;      // workspace [ceil(B/32)][rank/64] arrival counts, zero between calls
     int32_t batch, hidden, rank, nq, ksplit;
     float eps;
+};
+
+// The fused RMSNorm keeps one sum of squares per 64-column block of the
+// bottleneck per row in LDS: q_rank <= 64 * kMaxNormBlocks.
+constexpr int kMaxNormBlocks = 64;
+
+// Epilogues of the skinny GEMM (see mfa_skinny_gemm_kernel).
+enum { kEpiPartials = 0, kEpiBf16 = 1, kEpiNormPrep = 2, kEpiBf16RowScale = 3 };
+struct GemmEpi {
+    const uint16_t* gamma;
+    uint16_t* cg;
+    float* sumsq;
+    int32_t* counters;
+    float eps;
+    int32_t rank;
 };
 
 // The down-projection splits K into blocks of this many rows (one
@@ -107,7 +124,6 @@ hipError_t launch_kv_proj(const KvAppendArgs& a, const Launch& l);
 hipError_t launch_kv_write(const KvAppendArgs& a, bool fp8, bool paged, const Launch& l);
 
 hipError_t launch_qproj_down(const QprojArgs& a, const Launch& l);
-hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l);
 hipError_t launch_qproj_up(const QprojArgs& a, const Launch& l);
 
 }  // namespace mfa

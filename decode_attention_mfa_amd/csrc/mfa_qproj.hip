@@ -2,9 +2,12 @@
 // hidden -> 2048-wide bottleneck -> 64 heads x 256 ("Step-3 is Large yet
 // Affordable", Key points), with RMSNorm on the bottleneck.
 //
-//   down   c_part[split] = x . W_qa[k-range]      skinny bf16 MFMA GEMM, fp32
-//   norm   chat = bf16(sum_split c_part * rsqrt(mean(c^2) + eps) * gamma)
-//   up     q = bf16(chat . W_qb)                   skinny bf16 MFMA GEMM
+//   down   c_part[split] = x . W_qa[k-range]      skinny bf16 MFMA GEMM, fp32;
+//          the last K split to finish a column block sums the partials in
+//          split order and writes cg = bf16(c * gamma) and the block's
+//          per-row sums of c^2
+//   up     q = bf16(rsqrt(mean(c^2) + eps) * (cg . W_qb))   skinny bf16 MFMA
+//          GEMM, the RMSNorm factor applied per row to the fp32 result
 //
 // The same skinny GEMM also computes the new token's key and value rows,
 // x . W_k and x . W_v (hidden -> 256 each, one launch for both weights), for
@@ -62,6 +65,25 @@ __device__ __forceinline__ void wait_vmem() {
 // LDS-only workgroup barrier (does not wait for the DMA still in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Eight device-coherent (sc1, agent scope) 16-byte loads, p[i] -> v[i],
+// issued together; the asm block also waits for them, so no output register
+// is left pending when it ends.
+__device__ __forceinline__ void coherent_load_b128x8(f32x4* v, const f32x4* const* p) {
+    asm volatile(
+        "global_load_dwordx4 %0, %8, off sc1\n\t"
+        "global_load_dwordx4 %1, %9, off sc1\n\t"
+        "global_load_dwordx4 %2, %10, off sc1\n\t"
+        "global_load_dwordx4 %3, %11, off sc1\n\t"
+        "global_load_dwordx4 %4, %12, off sc1\n\t"
+        "global_load_dwordx4 %5, %13, off sc1\n\t"
+        "global_load_dwordx4 %6, %14, off sc1\n\t"
+        "global_load_dwordx4 %7, %15, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+        : "memory");
+}
+
 __device__ __forceinline__ const uint8_t* uniform_ptr(const void* ptr) {
     const uint64_t u = (uint64_t)(uintptr_t)ptr;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
@@ -77,12 +99,21 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* ptr) {
 // X . W2 into Y2 with the blocks bx >= N/64 (bx - N/64 there).
 // MR (32 or 64) rows per block: 32 when the batch fits, so that the
 // activation tile carries no repeated rows.
-// OUT_BF16: Y is bf16 [M][N]; otherwise fp32 partials [gridDim.y][M][N].
-template <bool OUT_BF16, int MR>
+// EPI selects the output:
+//   kEpiPartials  fp32 partials [gridDim.y][M][N] in Y;
+//   kEpiBf16      bf16 [M][N] in Y;
+//   kEpiNormPrep  partials as kEpiPartials, then the last K split to finish
+//                 column block bx (counted in e.counters) sums them in split
+//                 order: e.cg[m][n] = bf16(c * gamma[n]) and e.sumsq[m][bx] =
+//                 sum over the block's 64 columns of c^2;
+//   kEpiBf16RowScale  bf16(acc * r[m]) in Y, r[m] = rsqrt(sum_j e.sumsq[m][j]
+//                 / e.rank + e.eps) over the e.rank / 64 column blocks j.
+template <int EPI, int MR>
 __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __restrict__ X, int ldx,
                                                               const uint16_t* __restrict__ W, int N, int kper,
                                                               int M, void* __restrict__ Y,
-                                                              const uint16_t* __restrict__ W2, void* __restrict__ Y2) {
+                                                              const uint16_t* __restrict__ W2, void* __restrict__ Y2,
+                                                              const GemmEpi e) {
     static_assert(MR == 32 || MR == 64, "rows per block");
     constexpr int MT = MR / 16;            // 16-row MFMA tiles
     constexpr int XI = MR / 32;            // activation DMA instructions per wave and tile
@@ -121,6 +152,23 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
         const int r = MR / 4 * w + 8 * i + (l >> 3);
         const int xr = min(m0 + r, M - 1) - m0;   // row within this block
         xoff[i] = (uint32_t)(xr * ldx * 2 + 16 * ((l & 7) ^ xswz(r)));
+    }
+    // kEpiBf16RowScale: the block's rows of e.sumsq ([M][nb] fp32, nb =
+    // rank/64 <= kMaxNormBlocks) are copied into LDS by 4-byte DMA ahead of the
+    // ring, so they are older than every tile load and the ring's waits cover
+    // them; element idx of the copy is row idx / nb (rows past M repeat row
+    // M-1, in bounds), column idx % nb.
+    __shared__ float ss_lds[EPI == kEpiBf16RowScale ? MR * kMaxNormBlocks : 1];
+    if constexpr (EPI == kEpiBf16RowScale) {
+        const int nb = e.rank / 64;
+        const uint8_t* sb = uniform_ptr(e.sumsq);
+        for (int i = w; i * 64 < MR * nb; i += 4) {
+            const int idx = 64 * i + l;
+            const int r = min(min(idx / nb, MR - 1) + m0, M - 1);
+            const uint32_t off = (uint32_t)((r * nb + idx % nb) * 4);
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr_of(ss_lds) + 256 * i);
+            asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(sb), "{m0}"(dst) : "memory");
+        }
     }
     auto issue = [&](int tile) {   // clamped to the last tile
         const int k0 = kbeg + 64 * min(tile, ntiles - 1);
@@ -176,6 +224,20 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
     wait_vmem<0>();   // the clamped loads past the last tile
 
     const int n = n0 + 16 * w + lr;
+    __shared__ float row_scale[MR];
+    __shared__ int arrival;
+    if constexpr (EPI == kEpiBf16RowScale) {
+        // the RMSNorm factor of this block's rows, from the column blocks'
+        // sums of squares (every wave's copy has landed: wait above, barrier)
+        __syncthreads();
+        if (tid < MR) {
+            const int nb = e.rank / 64;
+            float ss = 0.f;
+            for (int j = 0; j < nb; j++) ss += ss_lds[tid * nb + j];
+            row_scale[tid] = 1.0f / __builtin_sqrtf(ss / (float)e.rank + e.eps);
+        }
+        __syncthreads();
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
         if (mt >= mt_n) continue;
@@ -183,91 +245,102 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
         for (int i = 0; i < 4; i++) {
             const int m = m0 + 16 * mt + 4 * g + i;
             if (m >= M) continue;
-            if constexpr (OUT_BF16) {
+            if constexpr (EPI == kEpiBf16) {
                 reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = bitcast<uint16_t>((__bf16)acc[mt][i]);
-            } else {
+            } else if constexpr (EPI == kEpiBf16RowScale) {
+                const float v = acc[mt][i] * row_scale[m - m0];
+                reinterpret_cast<uint16_t*>(Y)[(int64_t)m * N + n] = bitcast<uint16_t>((__bf16)v);
+            } else if constexpr (EPI == kEpiPartials) {
                 reinterpret_cast<float*>(Y)[((int64_t)blockIdx.y * M + m) * N + n] = acc[mt][i];
+            } else {
+                // device-coherent: the summing workgroup may run on another XCD
+                __hip_atomic_store(reinterpret_cast<float*>(Y) + ((int64_t)blockIdx.y * M + m) * N + n, acc[mt][i],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
-}
-
-// chat[m][j] = bf16(c[m][j] * rsqrt(mean_j c^2 + eps) * gamma[j]), with
-// c = the sum of the K-split partials in split order. Block = one row m;
-// thread t handles columns 4t + 1024q. Each pass issues the loads of eight
-// splits of a column group before summing them.
-__global__ __launch_bounds__(256) void mfa_rmsnorm_kernel(const float* __restrict__ c_part, int ksplit, int M,
-                                                          int rank, const uint16_t* __restrict__ gamma, float eps,
-                                                          uint16_t* __restrict__ chat) {
-    __shared__ float red[4];
-    const int m = blockIdx.x;
-    const f32x4* cp = reinterpret_cast<const f32x4*>(c_part) + (int64_t)m * (rank / 4);
-    const int64_t plane = (int64_t)M * (rank / 4);   // f32x4 per split plane
-    auto col_sum = [&](int j4) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-        int s = 0;
-        for (; s + 8 <= ksplit; s += 8) {
-            f32x4 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; u++) v[u] = cp[(s + u) * plane + j4];
-#pragma unroll
-            for (int u = 0; u < 8; u++) c += v[u];
-        }
-        for (; s < ksplit; s++) c += cp[s * plane + j4];
-        return c;
-    };
-    float ss = 0.f;
-    for (int j4 = threadIdx.x; j4 < rank / 4; j4 += 256) {
-        const f32x4 c = col_sum(j4);
-        ss += (c[0] * c[0] + c[1] * c[1]) + (c[2] * c[2] + c[3] * c[3]);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-    const float r = 1.0f / __builtin_sqrtf(tot / (float)rank + eps);
-    for (int j4 = threadIdx.x; j4 < rank / 4; j4 += 256) {
-        const f32x4 c = col_sum(j4);
-        const u32x2 gw = *reinterpret_cast<const u32x2*>(gamma + 4 * j4);
+    if constexpr (EPI == kEpiNormPrep) {
+        // every store of this workgroup is acknowledged before it counts
+        wait_vmem<0>();
+        __syncthreads();
+        int* const ctr = e.counters + blockIdx.z * (N / 64) + bx;
+        if (tid == 0) arrival = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (arrival != (int)gridDim.y - 1) return;
+        if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // last split: pass pp, thread t sums columns n0 + 4(t % 16) .. +4 of
+        // row m0 + 16 pp + t / 16 over the splits, in split order, eight
+        // 16-byte coherent loads at a time
+        const int nsplit = gridDim.y;
+        const int64_t plane4 = (int64_t)M * N / 4;   // f32x4 per split plane
+        const int c4 = tid & 15;
+        const int col = n0 + 4 * c4;
+        const u32x2 gw = *reinterpret_cast<const u32x2*>(e.gamma + col);
         const float g0 = __builtin_bit_cast(float, gw.x << 16), g1 = __builtin_bit_cast(float, gw.x & 0xffff0000u);
         const float g2 = __builtin_bit_cast(float, gw.y << 16), g3 = __builtin_bit_cast(float, gw.y & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(chat + (int64_t)m * rank + 4 * j4) =
-            u32x2{pack_bf16x2(c[0] * r * g0, c[1] * r * g1), pack_bf16x2(c[2] * r * g2, c[3] * r * g3)};
+#pragma unroll
+        for (int pp = 0; pp < MR / 16; pp++) {
+            const int m = m0 + 16 * pp + (tid >> 4);
+            const bool live = m < M;
+            const f32x4* src = reinterpret_cast<const f32x4*>(Y) + ((int64_t)min(m, M - 1) * N + col) / 4;
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < nsplit; s0 += 8) {
+                const f32x4* ptr[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++) ptr[u] = src + min(s0 + u, nsplit - 1) * plane4;
+                f32x4 v[8];
+                coherent_load_b128x8(v, ptr);
+#pragma unroll
+                for (int u = 0; u < 8; u++)
+                    if (s0 + u < nsplit) c += v[u];
+            }
+            if (live)
+                *reinterpret_cast<u32x2*>(e.cg + (int64_t)m * N + col) =
+                    u32x2{pack_bf16x2(c[0] * g0, c[1] * g1), pack_bf16x2(c[2] * g2, c[3] * g3)};
+            // sum of c^2 over the block's 64 columns: the 16 threads of the row
+            float ss = (c[0] * c[0] + c[1] * c[1]) + (c[2] * c[2] + c[3] * c[3]);
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+            if (live && c4 == 0) e.sumsq[(int64_t)m * (N / 64) + bx] = ss;
+        }
     }
 }
 
 // Rows per block: 32 when the whole batch fits in one such block, else 64.
-template <bool OUT_BF16>
+template <int EPI>
 static hipError_t launch_skinny(int gx, int gy, const uint16_t* X, int ldx, const uint16_t* W, int N, int kper,
-                                int M, void* Y, const uint16_t* W2, void* Y2, const Launch& l) {
+                                int M, void* Y, const uint16_t* W2, void* Y2, const GemmEpi& e, const Launch& l) {
     if (M <= 32)
-        return launch_kernel(mfa_skinny_gemm_kernel<OUT_BF16, 32>, dim3(gx, gy, 1), dim3(256), l, X, ldx, W, N,
-                             kper, M, Y, W2, Y2);
-    return launch_kernel(mfa_skinny_gemm_kernel<OUT_BF16, 64>, dim3(gx, gy, (M + 63) / 64), dim3(256), l, X, ldx,
-                         W, N, kper, M, Y, W2, Y2);
+        return launch_kernel(mfa_skinny_gemm_kernel<EPI, 32>, dim3(gx, gy, 1), dim3(256), l, X, ldx, W, N, kper, M,
+                             Y, W2, Y2, e);
+    return launch_kernel(mfa_skinny_gemm_kernel<EPI, 64>, dim3(gx, gy, (M + 63) / 64), dim3(256), l, X, ldx, W, N,
+                         kper, M, Y, W2, Y2, e);
 }
 
 hipError_t launch_qproj_down(const QprojArgs& a, const Launch& l) {
-    return launch_skinny<false>(a.rank / 64, a.ksplit, a.x, a.hidden, a.w_qa, a.rank, a.hidden / a.ksplit, a.batch,
-                                (void*)a.c_part, nullptr, nullptr, l);
-}
-
-hipError_t launch_rmsnorm(const QprojArgs& a, const Launch& l) {
-    return launch_kernel(mfa_rmsnorm_kernel, dim3(a.batch), dim3(256), l, (const float*)a.c_part, a.ksplit, a.batch,
-                         a.rank, a.rms_w, a.eps, a.chat);
+    GemmEpi e{};
+    e.gamma = a.rms_w;
+    e.cg = a.chat;
+    e.sumsq = a.sumsq;
+    e.counters = a.counters;
+    return launch_skinny<kEpiNormPrep>(a.rank / 64, a.ksplit, a.x, a.hidden, a.w_qa, a.rank, a.hidden / a.ksplit,
+                                       a.batch, (void*)a.c_part, nullptr, nullptr, e, l);
 }
 
 hipError_t launch_qproj_up(const QprojArgs& a, const Launch& l) {
-    return launch_skinny<true>(a.nq / 64, 1, a.chat, a.rank, a.w_qb, a.nq, a.rank, a.batch, (void*)a.q_out, nullptr,
-                               nullptr, l);
+    GemmEpi e{};
+    e.sumsq = a.sumsq;
+    e.rank = a.rank;
+    e.eps = a.eps;
+    return launch_skinny<kEpiBf16RowScale>(a.nq / 64, 1, a.chat, a.rank, a.w_qb, a.nq, a.rank, a.batch,
+                                           (void*)a.q_out, nullptr, nullptr, e, l);
 }
 
 hipError_t launch_kv_proj(const KvAppendArgs& a, const Launch& l) {
     float* kp = a.kv_part;
     float* vp = a.kv_part + (int64_t)a.ksplit * a.batch * kHeadDim;
-    return launch_skinny<false>(2 * kHeadDim / 64, a.ksplit, a.x, a.hidden, a.w_k, kHeadDim, a.hidden / a.ksplit,
-                                a.batch, (void*)kp, a.w_v, (void*)vp, l);
+    return launch_skinny<kEpiPartials>(2 * kHeadDim / 64, a.ksplit, a.x, a.hidden, a.w_k, kHeadDim,
+                                       a.hidden / a.ksplit, a.batch, (void*)kp, a.w_v, (void*)vp, GemmEpi{}, l);
 }
 
 }  // namespace mfa

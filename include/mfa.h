@@ -64,7 +64,7 @@ typedef struct mfa_ctx* mfa_handle;
 /* Layer configuration (host struct, copied by mfa_create). */
 typedef struct {
     int32_t hidden;        /* model width, 7168; multiple of 512 */
-    int32_t q_rank;        /* query bottleneck, 2048; multiple of 64 */
+    int32_t q_rank;        /* query bottleneck, 2048; multiple of 64, at most 4096 */
     int32_t num_heads;     /* query heads, must be 64 */
     int32_t head_dim;      /* must be 256 */
     int32_t kv_dtype;      /* enum mfa_kv_dtype */
@@ -112,8 +112,10 @@ typedef struct {
  *   chunk partials, C = split_tokens when positive, else 256 (the smallest
  *   piece a per-call choice or a balanced split makes), max_batch 4-byte arrival counters (zeroed here, left
  *   at zero by every call), Q-projection scratch of
- *   max_batch * q_rank * (4 * hidden / 512 + 2) bytes, and K/V-projection
- *   partials of 2 * (hidden / 256) * max_batch * 256 * 4 bytes.
+ *   max_batch * q_rank * (4 * hidden / 512 + 2) + (q_rank / 64) * (max_batch
+ *   + ceil(max_batch / 32)) * 4 bytes (its arrival counters zeroed here and
+ *   left at zero), and K/V-projection partials of
+ *   2 * (hidden / 256) * max_batch * 256 * 4 bytes.
  * On success stores the handle in *out (host pointer) and returns MFA_OK. */
 int mfa_create(const mfa_config* cfg, mfa_handle* out);
 
@@ -124,8 +126,10 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out);
  *                                           w_qa [hidden][q_rank] bf16
  *   chat = c * rsqrt(mean(c^2) + rms_eps) * rms_w      rms_w [q_rank] bf16
  *   q    = chat . w_qb                      w_qb [q_rank][64*256] bf16
- * q_out is [batch][64][256] bf16 (= [batch][16384]); c accumulates in fp32,
- * chat is rounded to bf16 before the second product.
+ * q_out is [batch][64][256] bf16 (= [batch][16384]); c accumulates in fp32;
+ * c * rms_w is rounded to bf16 before the second product, whose fp32 result
+ * is multiplied by the row's rsqrt(mean(c^2) + rms_eps) before rounding
+ * (the same product, the norm factor applied after it).
  * 1 <= batch <= max_batch. */
 int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
               const void* w_qb, void* q_out, int32_t batch, void* hip_stream);
@@ -204,7 +208,8 @@ enum mfa_kernel_kind {
     MFA_KERNEL_ATTENTION = 0,   /* chunked decode attention */
     MFA_KERNEL_COMBINE = 1,     /* log-sum-exp merge of chunk partials */
     MFA_KERNEL_QPROJ_DOWN = 2,  /* x . w_qa */
-    MFA_KERNEL_RMSNORM = 3,     /* bottleneck RMSNorm */
+    MFA_KERNEL_RMSNORM = 3,     /* (not launched: the RMSNorm is split between the two
+                                   projection kernels) */
     MFA_KERNEL_QPROJ_UP = 4,    /* chat . w_qb */
     MFA_KERNEL_KV_PROJ = 5,     /* x . w_k and x . w_v (K-split partials) */
     MFA_KERNEL_KV_WRITE = 6,    /* partial sums, encoding and the row write */
