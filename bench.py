@@ -186,6 +186,8 @@ def main():
                     help="untimed steps first; default: as many as take %.1f s" % 0.5)
     ap.add_argument("--workload", default="fp8_contig", choices=sorted(WORKLOADS))
     ap.add_argument("--split", type=int, default=None, help="override the split-K chunk (tokens)")
+    ap.add_argument("--attn-math", default="bf16", choices=("bf16", "fp8"),
+                    help="attention arithmetic: bf16 MFMAs (default) or FP8 MFMAs (FP8 caches only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget; 0 skips it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (for HBM counter scaling)")
@@ -249,7 +251,9 @@ def main():
     attn_lens = dc.seq_lens + 1 if append else dc.seq_lens
     attn_max = dc.max_len + 1 if append else dc.max_len
     attn_min = dc.min_len + 1 if append else dc.min_len
-    h = harness.create_handle(dc, split_tokens=args.split, max_context=attn_max, max_batch=dc.batch * qtok)
+    attn_math = mfa.MFA_ATTN_FP8_MFMA if args.attn_math == "fp8" else mfa.MFA_ATTN_BF16_MFMA
+    h = harness.create_handle(dc, split_tokens=args.split, max_context=attn_max, max_batch=dc.batch * qtok,
+                              attn_math=attn_math)
     # multi-token decode uses the chunked split, sized for batch x tokens rows
     split = mfa.mfa_split_tokens(h, dc.batch * qtok, attn_max, attn_max if qtok > 1 else attn_min)
     stream = torch.cuda.Stream()
@@ -328,6 +332,7 @@ def main():
                    "kv_dtype": "fp8_e4m3" if case.kv_dtype == "fp8" else "bf16",
                    "layout": "paged64" if case.paged else "contiguous", "split_tokens": split,
                    "query_tokens": qtok,
+                   "attn_math": "fp8 MFMA (quantised Q and P)" if args.attn_math == "fp8" else "bf16 MFMA",
                    "work_split": "balanced ranges of steps" if split == 0 else f"chunks of {split} tokens",
                    "input_sets_rotated": nrot, "mall": "cold" if cold else "warm"},
         "step_hbm_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),

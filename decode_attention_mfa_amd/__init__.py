@@ -24,6 +24,8 @@ MFA_ERR_HIP = -4
 MFA_DTYPE_BF16 = 0
 MFA_DTYPE_FP8_E4M3 = 1
 MFA_SPLIT_BALANCED = -1
+MFA_ATTN_BF16_MFMA = 0
+MFA_ATTN_FP8_MFMA = 1
 KERNEL_KINDS = ("attention", "combine", "qproj_down", "rmsnorm", "qproj_up", "kv_proj", "kv_write")
 
 
@@ -39,7 +41,7 @@ class mfa_config(ctypes.Structure):
                 ("kv_dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("max_batch", ctypes.c_int32), ("max_context", ctypes.c_int32),
                 ("split_tokens", ctypes.c_int32), ("rms_eps", ctypes.c_float),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("attn_math", ctypes.c_int32)]
 
 
 class mfa_kv(ctypes.Structure):
@@ -121,11 +123,11 @@ def mfa_last_error() -> str:
 
 def make_config(*, hidden=7168, q_rank=2048, num_heads=64, head_dim=256, kv_dtype=MFA_DTYPE_BF16,
                 page_size=0, max_batch=1, max_context=4096, split_tokens=0, rms_eps=1e-6,
-                softmax_scale=1.0 / 16.0) -> mfa_config:
+                softmax_scale=1.0 / 16.0, attn_math=MFA_ATTN_BF16_MFMA) -> mfa_config:
     if isinstance(kv_dtype, str):
         kv_dtype = MFA_DTYPE_FP8_E4M3 if kv_dtype == "fp8" else MFA_DTYPE_BF16
     return mfa_config(hidden, q_rank, num_heads, head_dim, kv_dtype, page_size, max_batch,
-                      max_context, split_tokens, rms_eps, softmax_scale)
+                      max_context, split_tokens, rms_eps, softmax_scale, attn_math)
 
 
 def make_kv(k, v, seq_lens, *, page_table=None, k_scale=1.0, v_scale=1.0, kv_stride=0,

@@ -175,6 +175,10 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
         return fail(MFA_ERR_INVALID, "mfa_create: softmax_scale must be finite and > 0");
     if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))
         return fail(MFA_ERR_INVALID, "mfa_create: rms_eps must be finite and >= 0");
+    if (c.attn_math != MFA_ATTN_BF16_MFMA && c.attn_math != MFA_ATTN_FP8_MFMA)
+        return fail(MFA_ERR_INVALID, "mfa_create: bad attn_math %d", c.attn_math);
+    if (c.attn_math == MFA_ATTN_FP8_MFMA && c.kv_dtype != MFA_DTYPE_FP8_E4M3)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: attn_math FP8_MFMA needs an FP8 cache");
 
     const int min_chunk = c.split_tokens > 0 ? c.split_tokens : kMinAutoSplit;
     const int64_t max_chunks = ((int64_t)c.max_context + min_chunk - 1) / min_chunk;
@@ -348,6 +352,8 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
     int32_t max_len = 0;
     int rc = check_kv(h, kv, batch, fn, &max_len);
     if (rc) return rc;
+    if (qtok > 1 && h->cfg.attn_math == MFA_ATTN_FP8_MFMA)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: multi-token decode runs with bf16 MFMAs only", fn);
     const int32_t rows = batch * qtok;   // query-row sets (one per sequence and token)
     if (rows > h->cfg.max_batch)
         return fail(MFA_ERR_INVALID, "%s: batch %d x num_tokens %d exceeds max_batch %d", fn, batch, qtok,
@@ -363,6 +369,7 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
     a.counters = h->counters;
     a.batch = batch;
     a.qtok = qtok;
+    a.fp8_mma = h->cfg.attn_math == MFA_ATTN_FP8_MFMA ? 1 : 0;
     int workgroups;
     if (qtok == 1 && use_balanced(h, batch, max_len, kv->min_seq_len)) {
         // equal ranges of at least 4 and at most 128 steps: one workgroup per

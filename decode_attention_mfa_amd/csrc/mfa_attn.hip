@@ -53,6 +53,8 @@ __device__ __forceinline__ int kswz(int t) { return t & 15; }
 template <bool FP8>
 __device__ __forceinline__ int vswz(int r) { return FP8 ? (r & 7) : ((r & 3) << 1); }
 __device__ __forceinline__ int pswz(int h) { return (h >> 1) & 7; }
+// FP8-MFMA mode: P as E4M3, 64-byte rows (64 tokens), 16-byte chunks
+__device__ __forceinline__ int p8swz(int h) { return (h >> 2) & 3; }
 
 // LDS stores issued as inline asm. The compiler treats a plain LDS store as
 // possibly overwriting bytes an LDS DMA is still filling and would first wait
@@ -153,7 +155,7 @@ __device__ __forceinline__ void wait_vmem() {
 // them on one XCD at about the same time: the KV bytes come from HBM once and
 // from that XCD's L2 for the other tokens.
 
-template <bool FP8, bool PAGED, bool MTP>
+template <bool FP8, bool PAGED, bool MTP, bool F8MMA>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mfa_attn_split_kernel(const AttnArgs p) {
 #define MFA_PIECE_TID threadIdx.x
@@ -216,7 +218,7 @@ __device__ __forceinline__ int opaque_thread_index() {
 // One piece of the balanced kernel: tokens [t_begin, t_end) of sequence b
 // (length L, t_begin < L), the piece_k-th of the sequence's nparts pieces,
 // whose partials sit at workspace slots part_base + 0 .. nparts-1.
-template <bool FP8, bool PAGED>
+template <bool FP8, bool PAGED, bool F8MMA>
 __device__ __forceinline__ void attend_piece(const AttnArgs& p, const int b, const int L, const int t_begin,
                                              const int t_end, const int piece_k, const int nparts,
                                              const int64_t part_base) {
@@ -246,7 +248,7 @@ __device__ __forceinline__ void write_empty(const AttnArgs& p, int b) {
     if (p.lse_out && threadIdx.x < kHeads) p.lse_out[b * kHeads + threadIdx.x] = -__builtin_inff();
 }
 
-template <bool FP8, bool PAGED>
+template <bool FP8, bool PAGED, bool F8MMA>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mfa_attn_balanced_kernel(const AttnArgs p) {
     __shared__ int wave_total[4];
@@ -330,7 +332,7 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
             if (n > 0) {
                 const int seg_end = min(s_hi, Pq + n);
                 const int first = Pq / per, last = (Pq + n - 1) / per;
-                attend_piece<FP8, PAGED>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
+                attend_piece<FP8, PAGED, F8MMA>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
                                          (int)blockIdx.x - first, last - first + 1, (int64_t)bq * p.part_stride);
                 s = seg_end;
                 if (s >= s_hi) break;
@@ -432,25 +434,32 @@ __global__ __launch_bounds__(256) void mfa_gather_kernel(const KvView kv, int b,
 
 hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l) {
     const dim3 grid(workgroups), block(256);
+    if (a.fp8_mma) {   // FP8 cache only (checked by the caller)
+        if (a.balanced)
+            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, true>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_balanced_kernel<true, false, true>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_split_kernel<true, true, false, true>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_split_kernel<true, false, false, true>, grid, block, l, a);
+    }
     if (a.balanced) {
         if (fp8)
-            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true>, grid, block, l, a)
-                         : launch_kernel(mfa_attn_balanced_kernel<true, false>, grid, block, l, a);
-        return paged ? launch_kernel(mfa_attn_balanced_kernel<false, true>, grid, block, l, a)
-                     : launch_kernel(mfa_attn_balanced_kernel<false, false>, grid, block, l, a);
+            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, false>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_balanced_kernel<true, false, false>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_balanced_kernel<false, true, false>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_balanced_kernel<false, false, false>, grid, block, l, a);
     }
     if (a.qtok > 1) {
         if (fp8)
-            return paged ? launch_kernel(mfa_attn_split_kernel<true, true, true>, grid, block, l, a)
-                         : launch_kernel(mfa_attn_split_kernel<true, false, true>, grid, block, l, a);
-        return paged ? launch_kernel(mfa_attn_split_kernel<false, true, true>, grid, block, l, a)
-                     : launch_kernel(mfa_attn_split_kernel<false, false, true>, grid, block, l, a);
+            return paged ? launch_kernel(mfa_attn_split_kernel<true, true, true, false>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_split_kernel<true, false, true, false>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_split_kernel<false, true, true, false>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_split_kernel<false, false, true, false>, grid, block, l, a);
     }
     if (fp8)
-        return paged ? launch_kernel(mfa_attn_split_kernel<true, true, false>, grid, block, l, a)
-                     : launch_kernel(mfa_attn_split_kernel<true, false, false>, grid, block, l, a);
-    return paged ? launch_kernel(mfa_attn_split_kernel<false, true, false>, grid, block, l, a)
-                 : launch_kernel(mfa_attn_split_kernel<false, false, false>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_split_kernel<true, true, false, false>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_split_kernel<true, false, false, false>, grid, block, l, a);
+    return paged ? launch_kernel(mfa_attn_split_kernel<false, true, false, false>, grid, block, l, a)
+                 : launch_kernel(mfa_attn_split_kernel<false, false, false, false>, grid, block, l, a);
 }
 
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l) {

@@ -28,6 +28,10 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // before the chunk is redone with a higher reference: unnormalised P stays
 // <= 2^kTau, so with |V| < 2^64 the fp32 accumulators cannot overflow.
 constexpr float kTau = 48.0f;
+// With FP8 P (the FP8-MFMA mode) the excess is bounded by 2^6, so that P * 4
+// stays below E4M3's 448 (and a restart stays rare: the later scores of a
+// piece seldom exceed its first step's maxima by six octaves).
+constexpr float kTauF8 = 6.0f;
 
 template <typename T, typename S>
 __device__ __forceinline__ T bitcast(const S& s) {
@@ -39,6 +43,19 @@ __device__ __forceinline__ T bitcast(const S& s) {
 // B[8*(l/16)+j][l%16] (j = 0..7) and D[4*(l/16)+i][l%16] (i = 0..3).
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// FP8 (E4M3 x E4M3) MFMAs, unscaled: 16x16x128 (A: lane l holds row l%16,
+// k = 32(l/16) + byte; B the same with column l%16; C as mfma16) and
+// 32x32x64 (A: row l%32, k = 32(l/32) + byte; C: lane l holds column l%32,
+// rows 8(i/4) + 4(l/32) + i%4 for i < 16).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x4 mfma16_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // Four E4M3FN codes (one dword, byte 0 first) -> four bf16, exactly: every

@@ -41,6 +41,7 @@ struct AttnArgs {
     int32_t balanced;       // 1: equal step ranges per workgroup (chunk, n_chunk unused)
     int32_t batch;          // cache sequences in the call (balanced and multi-token modes)
     int32_t qtok;           // query tokens per sequence (1, or t for multi-token decode)
+    int32_t fp8_mma;        // 1: FP8 MFMAs for S and P.V (quantised Q and P)
     int32_t part_stride;    // workspace partial slots per sequence (balanced mode)
 };
 

@@ -73,13 +73,13 @@ def to_device(case, device="cuda") -> DeviceCase:
 
 
 def create_handle(dc: DeviceCase, *, max_batch: Optional[int] = None, max_context: Optional[int] = None,
-                  split_tokens: Optional[int] = None) -> int:
+                  split_tokens: Optional[int] = None, attn_math: int = 0) -> int:
     return mfa_create(make_config(
         kv_dtype=MFA_DTYPE_FP8_E4M3 if dc.kv_dtype == "fp8" else MFA_DTYPE_BF16,
         page_size=64 if dc.paged else 0, max_batch=max_batch or dc.batch,
         max_context=max_context or dc.max_len,
         split_tokens=dc.split_tokens if split_tokens is None else split_tokens,
-        rms_eps=dc.rms_eps, softmax_scale=dc.softmax_scale))
+        rms_eps=dc.rms_eps, softmax_scale=dc.softmax_scale, attn_math=attn_math))
 
 
 def alloc_outputs(dc: DeviceCase):

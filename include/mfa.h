@@ -52,6 +52,22 @@ enum mfa_kv_dtype {
     MFA_DTYPE_FP8_E4M3 = 1
 };
 
+/* Arithmetic of mfa_decode's scores and P.V (the FP8 deployment and its
+ * BF16-attention ablation in the Step-3 Key points):
+ *   MFA_ATTN_BF16_MFMA  bf16 MFMAs; FP8 codes are widened exactly to bf16, Q
+ *                       stays bf16, P is rounded to bf16 (the default).
+ *   MFA_ATTN_FP8_MFMA   FP8 (E4M3) MFMAs on the cache's codes: Q quantised
+ *                       per head to E4M3 (a power-of-two scale puts each
+ *                       head's largest |q| in [128, 256)), P quantised to
+ *                       E4M3 (scaled by 4); half the MFMA cycles, and about
+ *                       2^-4 relative rounding on every Q and P element (a
+ *                       normwise output error of a few percent on the
+ *                       workloads). FP8 caches only; not for mfa_decode_mtp. */
+enum mfa_attn_math {
+    MFA_ATTN_BF16_MFMA = 0,
+    MFA_ATTN_FP8_MFMA = 1
+};
+
 typedef struct mfa_ctx* mfa_handle;
 
 /* mfa_config.split_tokens value: cut the work of each call into equal ranges
@@ -77,6 +93,7 @@ typedef struct {
                               else chunks sized for the batch) */
     float rms_eps;         /* RMSNorm epsilon (1e-6), >= 0 */
     float softmax_scale;   /* score scale (1/16 = 1/sqrt(256)), finite and > 0 */
+    int32_t attn_math;     /* enum mfa_attn_math; MFA_ATTN_FP8_MFMA needs an FP8 cache */
 } mfa_config;
 
 /* KV cache of one layer for one call (host struct describing device buffers).

@@ -45,6 +45,9 @@ def _create(**kw):
     (dict(max_batch=0), -1, "max_batch"),
     (dict(split_tokens=100), -1, "split_tokens"),
     (dict(split_tokens=-2), -1, "split_tokens"),
+    (dict(attn_math=5), -1, "attn_math"),
+    (dict(attn_math=1, kv_dtype="bf16"), -2, "FP8 cache"),
+    (dict(q_rank=8192), -2, "q_rank"),
     (dict(page_size=64, split_tokens=8256), -2, "paged cache"),
     (dict(softmax_scale=0.0), -1, "softmax_scale"),
     (dict(softmax_scale=float("inf")), -1, "softmax_scale"),

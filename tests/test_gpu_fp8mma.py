@@ -1,0 +1,150 @@
+"""GPU parity of the FP8-MFMA attention mode (MFA_ATTN_FP8_MFMA: FP8 MFMAs on
+the cache's codes, Q quantised per head and P quantised to E4M3) against the
+exact fp64 oracle.
+
+This mode is an approximation with its own error budget: every Q element and
+every softmax weight carries up to 2^-4 relative rounding (E4M3's three
+mantissa bits), where the default path has bf16's 2^-9. A CPU model of the
+same arithmetic on the workloads' inputs gives a row-wise normwise error of
+6-12%. The log-sum-exp inherits the score error: a score is a sum of 256
+products each off by up to 2^-4 relative, about 0.036 (one standard
+deviation, natural-log units) for N(0,1) data; over a long context it
+averages out (0.015 seen), for a one-token context the LSE is that score
+(about 0.06 seen). The bars below leave room above both. The default
+(bf16-MFMA) path keeps the 1e-2 bar of the other tests.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL_F8 = 0.2        # row-wise normwise relative error
+LSE_TOL_F8 = 0.25   # absolute, natural log (about seven standard deviations of one score)
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _mfa():
+    import decode_attention_mfa_amd as m
+    from decode_attention_mfa_amd import harness
+    return m, harness
+
+
+def _run(case, split, attn_math):
+    m, hz = _mfa()
+    dc = hz.to_device(case)
+    h = hz.create_handle(dc, split_tokens=split, attn_math=attn_math)
+    try:
+        out, lse = hz.decode(h, dc)
+        torch.cuda.synchronize()
+    finally:
+        m.mfa_destroy(h)
+    return hz.bf16_to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def check_f8(case, split, label, tol=TOL_F8):
+    m, _ = _mfa()
+    _say(f"[fp8 mfma] {label}: B={case.batch} paged={case.paged} L=[{case.seq_lens.min()},"
+         f"{case.seq_lens.max()}] split={split}")
+    o, lse = _run(case, split, m.MFA_ATTN_FP8_MFMA)
+    o_ref, lse_ref = oracle.case_attention(case)
+    nz = case.seq_lens > 0
+    err = np.abs(o - o_ref).max(axis=-1) / np.maximum(np.abs(o_ref).max(axis=-1), 1e-30)
+    e = float(err[nz].max()) if nz.any() else 0.0
+    el = float(np.abs(lse[nz] - lse_ref[nz]).max()) if nz.any() else 0.0
+    _say(f"    row-rel err {e:.3e}  lse abs err {el:.3e}")
+    assert e <= tol and el <= LSE_TOL_F8
+    if (~nz).any():
+        assert np.all(o[~nz] == 0) and np.all(np.isneginf(lse[~nz]))
+    return o, lse
+
+
+@pytest.mark.parametrize("split", [0, 256, 1024])
+def test_fp8_mma_contiguous(split):
+    check_f8(synth.config_case(3, batch=3, scale_len=0.5), split, "fp8 contiguous B=3 L=2048")
+
+
+@pytest.mark.parametrize("split", [0, 128, -1])
+def test_fp8_mma_paged_ragged(split):
+    check_f8(synth.config_case(4, batch=24, scale_len=1 / 16), split, "paged ragged")
+
+
+def test_fp8_mma_ragged_tails_and_empty():
+    L = [0, 1, 63, 64, 65, 127, 129, 1000, 2049, 0]
+    case = synth.make_case("f8tails", len(L), L, "fp8", seed=120, kv_slack=3)
+    check_f8(case, 256, "ragged tails")
+    check_f8(case, -1, "ragged tails balanced")
+
+
+def test_fp8_mma_peaky_scores_restart():
+    """Q scaled by 4: later scores exceed the first step's maxima by more than
+    the FP8 mode's bound (2^6), so the pieces restart with raised references.
+    The score error grows with |q||k| (here up to 0.8 in base-2 units), and
+    with so few dominant tokens the output error is about 0.22 (the CPU model
+    of this arithmetic gives 0.23): the bar is raised accordingly."""
+    check_f8(synth.config_case(3, batch=2, scale_len=0.25, q_std=4.0), 256, "peaky q", tol=0.35)
+
+
+def test_fp8_mma_differs_from_bf16_path():
+    """The mode is really in effect (its rounding differs from the default
+    path's), and the default path stays within its own 1e-2 bar."""
+    m, _ = _mfa()
+    case = synth.config_case(3, batch=2, scale_len=0.25)
+    o8, _ = _run(case, 256, m.MFA_ATTN_FP8_MFMA)
+    o16, _ = _run(case, 256, m.MFA_ATTN_BF16_MFMA)
+    o_ref, _ = oracle.case_attention(case)
+    e16 = (np.abs(o16 - o_ref).max(axis=-1) / np.abs(o_ref).max(axis=-1)).max()
+    d = (np.abs(o8 - o16).max(axis=-1) / np.abs(o16).max(axis=-1)).max()
+    _say(f"[fp8 mfma] default path err {e16:.3e}, fp8 vs default {d:.3e}")
+    assert e16 <= 1e-2 and d > 1e-3
+
+
+def test_fp8_mma_rejected_where_unsupported():
+    m, hz = _mfa()
+    with pytest.raises(m.MfaError) as ei:
+        m.mfa_create(kv_dtype="bf16", attn_math=m.MFA_ATTN_FP8_MFMA)
+    assert ei.value.status == m.MFA_ERR_UNSUPPORTED and "FP8 cache" in str(ei.value)
+    case = synth.config_case(3, batch=1, scale_len=1 / 16)
+    dc = hz.to_device(case)
+    h = hz.create_handle(dc, max_batch=2, attn_math=m.MFA_ATTN_FP8_MFMA)
+    try:
+        q = torch.zeros((1, 2, 64, 256), dtype=torch.int16, device="cuda")
+        o = torch.empty_like(q)
+        with pytest.raises(m.MfaError) as ei:
+            m.mfa_decode_mtp(h, q, dc.kv(), 2, o, None, 1)
+        assert "bf16 MFMAs" in str(ei.value)
+    finally:
+        m.mfa_destroy(h)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_fp8_mma_full_size(cfg):
+    """The FP8 workloads at full size in the FP8-MFMA mode: sampled sequences
+    against the oracle."""
+    m, hz = _mfa()
+    case = synth.config_case(cfg)
+    _say(f"[fp8 mfma full size] workload {cfg}: B={case.batch}")
+    o, lse = _run(case, None, m.MFA_ATTN_FP8_MFMA)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    idx = np.unique(np.concatenate([np.linspace(0, case.batch - 1, 6).astype(int),
+                                    [int(np.argmin(case.seq_lens)), int(np.argmax(case.seq_lens))]]))
+    sub = synth.Case(name="s", batch=len(idx), kv_dtype="fp8", seq_lens=case.seq_lens[idx], k=None, v=None,
+                     q=case.q[idx], k_scale=case.k_scale, v_scale=case.v_scale)
+    if case.paged:
+        sub.k, sub.v, sub.page_table = case.k, case.v, case.page_table[idx]
+    else:
+        sub.k, sub.v = case.k[idx], case.v[idx]
+    o_ref, lse_ref = oracle.case_attention(sub)
+    err = np.abs(o[idx] - o_ref).max(axis=-1) / np.maximum(np.abs(o_ref).max(axis=-1), 1e-30)
+    el = np.abs(lse[idx] - lse_ref).max()
+    _say(f"    row-rel err {err.max():.3e}  lse abs err {el:.3e}")
+    assert err.max() <= TOL_F8 and el <= LSE_TOL_F8
