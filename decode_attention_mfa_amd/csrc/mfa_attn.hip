@@ -89,6 +89,15 @@ __device__ __forceinline__ void dma_b128(const void* sbase, uint32_t voff, uint3
     asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds_dst) : "memory");
 }
 
+// Device-coherent (sc1) variants for reading back data that workgroups on
+// other XCDs published with device-coherent stores: 16 or 4 bytes per lane.
+__device__ __forceinline__ void dma_b128_coherent(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("global_load_lds_dwordx4 %0, %1 sc1" ::"v"(voff), "s"(sbase), "{m0}"(lds_dst) : "memory");
+}
+__device__ __forceinline__ void dma_b32_coherent(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("global_load_lds_dword %0, %1 sc1" ::"v"(voff), "s"(sbase), "{m0}"(lds_dst) : "memory");
+}
+
 // A pointer every lane of the wave holds, moved to scalar registers.
 __device__ __forceinline__ const uint8_t* wave_uniform(const uint8_t* ptr) {
     const uint64_t u = (uint64_t)(uintptr_t)ptr;
@@ -206,6 +215,57 @@ void mfa_attn_split_kernel(const AttnArgs p) {
 #undef MFA_PIECE_BASE
 }
 
+// FP8 caches: the same work split, eight waves in two roles (the body in
+// mfa_attn_ws.inc).
+template <bool PAGED, bool MTP, bool F8MMA>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void mfa_attn_ws_split_kernel(const AttnArgs p) {
+    int b, c, kvb, L;
+    if constexpr (!MTP) {
+        b = blockIdx.x / p.n_chunk;
+        c = blockIdx.x - b * p.n_chunk;
+        kvb = b;
+        L = seq_len(p.kv, b);
+    } else {
+        const int t = p.qtok;
+        const int grp = blockIdx.x / (8 * t);
+        const int r = blockIdx.x - grp * 8 * t;
+        const int wi = grp * 8 + (r & 7);   // (sequence, chunk) work item
+        if (wi >= p.batch * p.n_chunk) return;
+        kvb = wi / p.n_chunk;
+        c = wi - kvb * p.n_chunk;
+        const int j = r >> 3;
+        b = kvb * t + j;
+        L = max(0, seq_len(p.kv, kvb) - (t - 1 - j));
+    }
+    const int t_begin = c * p.chunk;
+
+    if (t_begin >= L) {
+        if (c == 0) {  // empty sequence: out = 0, lse = -inf
+            uint16_t* ob = p.out + (int64_t)b * kHeads * kHeadDim;
+            for (int i = threadIdx.x; i < kHeads * kHeadDim / 8; i += 512)
+                reinterpret_cast<u32x4*>(ob)[i] = u32x4{0, 0, 0, 0};
+            if (p.lse_out && threadIdx.x < kHeads)
+                p.lse_out[b * kHeads + threadIdx.x] = -__builtin_inff();
+        }
+        return;
+    }
+    const int t_end = min(L, t_begin + p.chunk);
+    const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
+    const int last_s = nsteps - 1;
+    const bool single = (L + p.chunk - 1) / p.chunk == 1;
+
+#define MFA_PIECE_TID threadIdx.x
+#define MFA_PIECE_K c
+#define MFA_PIECE_NPARTS ((L + p.chunk - 1) / p.chunk)
+#define MFA_PIECE_BASE ((int64_t)b * p.n_chunk)
+#include "mfa_attn_ws.inc"
+#undef MFA_PIECE_TID
+#undef MFA_PIECE_K
+#undef MFA_PIECE_NPARTS
+#undef MFA_PIECE_BASE
+}
+
 // The thread index through an opaque copy: in the balanced kernel's piece
 // loop, values derived from it are then computed per piece instead of being
 // hoisted out of the loop, where they would stay live across the step loop.
@@ -218,6 +278,31 @@ __device__ __forceinline__ int opaque_thread_index() {
 // One piece of the balanced kernel: tokens [t_begin, t_end) of sequence b
 // (length L, t_begin < L), the piece_k-th of the sequence's nparts pieces,
 // whose partials sit at workspace slots part_base + 0 .. nparts-1.
+template <bool FP8, bool PAGED, bool F8MMA>
+__device__ __forceinline__ void attend_piece(const AttnArgs& p, const int b, const int L, const int t_begin,
+                                             const int t_end, const int piece_k, const int nparts,
+                                             const int64_t part_base);
+
+// FP8 caches: the wave-specialized body (512 threads).
+template <bool PAGED, bool F8MMA>
+__device__ __forceinline__ void attend_piece_ws(const AttnArgs& p, const int b, const int L, const int t_begin,
+                                                const int t_end, const int piece_k, const int nparts,
+                                                const int64_t part_base) {
+    const int kvb = b;
+    const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
+    const int last_s = nsteps - 1;
+    const bool single = nparts == 1;
+#define MFA_PIECE_TID opaque_thread_index()
+#define MFA_PIECE_K piece_k
+#define MFA_PIECE_NPARTS nparts
+#define MFA_PIECE_BASE part_base
+#include "mfa_attn_ws.inc"
+#undef MFA_PIECE_TID
+#undef MFA_PIECE_K
+#undef MFA_PIECE_NPARTS
+#undef MFA_PIECE_BASE
+}
+
 template <bool FP8, bool PAGED, bool F8MMA>
 __device__ __forceinline__ void attend_piece(const AttnArgs& p, const int b, const int L, const int t_begin,
                                              const int t_end, const int piece_k, const int nparts,
@@ -243,15 +328,18 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& p, const int b, con
 // out = 0, lse = -inf for an empty sequence.
 __device__ __forceinline__ void write_empty(const AttnArgs& p, int b) {
     uint16_t* ob = p.out + (int64_t)b * kHeads * kHeadDim;
-    for (int i = threadIdx.x; i < kHeads * kHeadDim / 8; i += 256)
+    for (int i = threadIdx.x; i < kHeads * kHeadDim / 8; i += blockDim.x)
         reinterpret_cast<u32x4*>(ob)[i] = u32x4{0, 0, 0, 0};
     if (p.lse_out && threadIdx.x < kHeads) p.lse_out[b * kHeads + threadIdx.x] = -__builtin_inff();
 }
 
 template <bool FP8, bool PAGED, bool F8MMA>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(FP8 ? 512 : 256, FP8 ? 512 : 256),
+                          amdgpu_waves_per_eu(FP8 ? 2 : 1, FP8 ? 2 : 1)))
 void mfa_attn_balanced_kernel(const AttnArgs p) {
-    __shared__ int wave_total[4];
+    constexpr int NT = FP8 ? 512 : 256;   // threads
+    constexpr int NW = NT / 64;           // waves
+    __shared__ int wave_total[NW];
     __shared__ int first_seq[3];
     __shared__ unsigned empty_mask;   // bit j: sequence blockIdx.x + j*G is empty
     const int tid = threadIdx.x;
@@ -265,7 +353,7 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
     // [t*per_t, (t+1)*per_t) (up to four lengths kept in registers, so
     // the lengths are read once), then a scan across the workgroup
     constexpr int kRegLens = 4;
-    const int per_t = (B + 255) / 256;
+    const int per_t = (B + NT - 1) / NT;
     const int b0 = min(B, tid * per_t), b1 = min(B, b0 + per_t);
     int lens[kRegLens];
     int cnt = 0;
@@ -303,7 +391,9 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
     __syncthreads();
     int excl = incl - cnt;
     for (int i = 0; i < w; i++) excl += wave_total[i];
-    const int total = ((wave_total[0] + wave_total[1]) + wave_total[2]) + wave_total[3];
+    int total = 0;
+#pragma unroll
+    for (int i = 0; i < NW; i++) total += wave_total[i];
     const int per = min(kMaxPagedChunkSteps, max(kMinBalancedSteps, (total + G - 1) / G));
     const int s_lo = blockIdx.x * per;
     const int s_hi = min(total, s_lo + per);
@@ -332,8 +422,14 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
             if (n > 0) {
                 const int seg_end = min(s_hi, Pq + n);
                 const int first = Pq / per, last = (Pq + n - 1) / per;
-                attend_piece<FP8, PAGED, F8MMA>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
-                                         (int)blockIdx.x - first, last - first + 1, (int64_t)bq * p.part_stride);
+                if constexpr (FP8)
+                    attend_piece_ws<PAGED, F8MMA>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
+                                                  (int)blockIdx.x - first, last - first + 1,
+                                                  (int64_t)bq * p.part_stride);
+                else
+                    attend_piece<FP8, PAGED, F8MMA>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
+                                                    (int)blockIdx.x - first, last - first + 1,
+                                                    (int64_t)bq * p.part_stride);
                 s = seg_end;
                 if (s >= s_hi) break;
                 __syncthreads();   // the piece is done with the LDS
@@ -433,31 +529,31 @@ __global__ __launch_bounds__(256) void mfa_gather_kernel(const KvView kv, int b,
 }
 
 hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l) {
-    const dim3 grid(workgroups), block(256);
+    const dim3 grid(workgroups), block(256), block_ws(512);
     if (a.fp8_mma) {   // FP8 cache only (checked by the caller)
         if (a.balanced)
-            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, true>, grid, block, l, a)
-                         : launch_kernel(mfa_attn_balanced_kernel<true, false, true>, grid, block, l, a);
-        return paged ? launch_kernel(mfa_attn_split_kernel<true, true, false, true>, grid, block, l, a)
-                     : launch_kernel(mfa_attn_split_kernel<true, false, false, true>, grid, block, l, a);
+            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, true>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_balanced_kernel<true, false, true>, grid, block_ws, l, a);
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true>, grid, block_ws, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, true>, grid, block_ws, l, a);
     }
     if (a.balanced) {
         if (fp8)
-            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, false>, grid, block, l, a)
-                         : launch_kernel(mfa_attn_balanced_kernel<true, false, false>, grid, block, l, a);
+            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, false>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_balanced_kernel<true, false, false>, grid, block_ws, l, a);
         return paged ? launch_kernel(mfa_attn_balanced_kernel<false, true, false>, grid, block, l, a)
                      : launch_kernel(mfa_attn_balanced_kernel<false, false, false>, grid, block, l, a);
     }
     if (a.qtok > 1) {
         if (fp8)
-            return paged ? launch_kernel(mfa_attn_split_kernel<true, true, true, false>, grid, block, l, a)
-                         : launch_kernel(mfa_attn_split_kernel<true, false, true, false>, grid, block, l, a);
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, true, false>, grid, block_ws, l, a);
         return paged ? launch_kernel(mfa_attn_split_kernel<false, true, true, false>, grid, block, l, a)
                      : launch_kernel(mfa_attn_split_kernel<false, false, true, false>, grid, block, l, a);
     }
     if (fp8)
-        return paged ? launch_kernel(mfa_attn_split_kernel<true, true, false, false>, grid, block, l, a)
-                     : launch_kernel(mfa_attn_split_kernel<true, false, false, false>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false>, grid, block_ws, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, false>, grid, block_ws, l, a);
     return paged ? launch_kernel(mfa_attn_split_kernel<false, true, false, false>, grid, block, l, a)
                  : launch_kernel(mfa_attn_split_kernel<false, false, false, false>, grid, block, l, a);
 }
