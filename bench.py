@@ -58,10 +58,19 @@ DESCRIPTION = {
 # sources that decide the attention kernel's memory traffic (kernel, launch
 # shape, split and merge policy); the stored HBM counters hold for this hash
 ATTN_SOURCES = ("decode_attention_mfa_amd/csrc/mfa_attn.hip", "decode_attention_mfa_amd/csrc/mfa_attn_piece_setup.inc",
-                "decode_attention_mfa_amd/csrc/mfa_attn_piece_run.inc", "decode_attention_mfa_amd/csrc/mfa_device.h",
+                "decode_attention_mfa_amd/csrc/mfa_attn_piece_run.inc", "decode_attention_mfa_amd/csrc/mfa_attn_ws.inc",
+                "decode_attention_mfa_amd/csrc/mfa_device.h",
                 "decode_attention_mfa_amd/csrc/mfa_internal.h", "decode_attention_mfa_amd/csrc/mfa_api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WARMUP_SECONDS = 0.5
+
+
+def attn_kernel_name(split: int, fp8: bool) -> str:
+    """The attention kernel a launch runs: balanced split, or chunks (FP8
+    caches take the eight-wave kernel)."""
+    if split == 0:
+        return "mfa_attn_balanced_kernel"
+    return "mfa_attn_ws_split_kernel" if fp8 else "mfa_attn_split_kernel"
 
 
 def log(*a):
@@ -166,6 +175,11 @@ def cpu_baseline(case, budget_s: float):
             "sample": f"{what} of the first {n} of {case.batch} sequences, fp64, {dt:.1f} s"}
 
 
+def traffic_key(workload: str, attn_math: str) -> str:
+    """Key of a workload's stored HBM counters (per attention arithmetic)."""
+    return workload if attn_math == "bf16" else f"{workload}/{attn_math}"
+
+
 def load_traffic(workload: str, sha: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -256,6 +270,7 @@ def main():
                               attn_math=attn_math)
     # multi-token decode uses the chunked split, sized for batch x tokens rows
     split = mfa.mfa_split_tokens(h, dc.batch * qtok, attn_max, attn_max if qtok > 1 else attn_min)
+    head_groups = mfa.mfa_head_groups(h, dc.batch * qtok, attn_max, attn_max if qtok > 1 else attn_min)
     stream = torch.cuda.Stream()
     if qtok > 1:
         outs = [(torch.empty((dc.batch, qtok, 64, 256), dtype=torch.int16, device="cuda"),
@@ -318,7 +333,7 @@ def main():
     attn_ms = ms_attn / max(n_attn, 1)
     achieved = attn_bytes / (attn_ms / 1e3) / 1e9
     sha = attn_source_sha()
-    traffic = load_traffic(wl, sha)
+    traffic = load_traffic(traffic_key(wl, args.attn_math), sha)
     kernels = {k: {"launches": n, "avg_us": round(ms * 1e3 / n, 2)} for k, (n, ms) in prof.items() if n}
 
     result = {
@@ -333,10 +348,11 @@ def main():
                    "layout": "paged64" if case.paged else "contiguous", "split_tokens": split,
                    "query_tokens": qtok,
                    "attn_math": "fp8 MFMA (quantised Q and P)" if args.attn_math == "fp8" else "bf16 MFMA",
-                   "work_split": "balanced ranges of steps" if split == 0 else f"chunks of {split} tokens",
+                   "work_split": ("balanced ranges of steps" if split == 0 else f"chunks of {split} tokens")
+                   + (", heads in two workgroups of 32" if head_groups == 2 else ""),
                    "input_sets_rotated": nrot, "mall": "cold" if cold else "warm"},
         "step_hbm_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": "mfa_attn_balanced_kernel" if split == 0 else "mfa_attn_split_kernel",
+        "roofline": {"bound": "hbm", "kernel": attn_kernel_name(split, case.kv_dtype == "fp8"),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": attn_bytes,

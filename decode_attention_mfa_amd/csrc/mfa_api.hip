@@ -55,7 +55,7 @@ struct mfa_ctx {
     int max_chunks;        // per sequence, at the smallest chunk this handle may use
     float* part_o;         // [max_batch * max_chunks][64][256]
     float* part_lse;       // [max_batch * max_chunks][64]
-    int32_t* counters;     // [max_batch], zero between calls
+    int32_t* counters;     // [max_batch][2], zero between calls
     float* c_part;         // [hidden / kQprojRowsPerSplit][max_batch][q_rank]
     uint16_t* chat;        // [max_batch][q_rank]: c * gamma, bf16
     float* sumsq;          // [max_batch][q_rank / 64]
@@ -117,16 +117,37 @@ static bool use_balanced(const mfa_ctx* h, int32_t batch, int32_t max_len, int32
     return !uniform;
 }
 
-static int32_t choose_split(const mfa_ctx* h, int32_t batch, int32_t max_len) {
+static int32_t choose_split(const mfa_ctx* h, int32_t batch, int32_t max_len, int32_t max_auto = kMaxAutoSplit) {
     if (h->cfg.split_tokens > 0) return h->cfg.split_tokens;
     if (max_len <= 0) return kMinAutoSplit;
     // one chunk per compute unit's share of the batch's tokens, whole pages
     int64_t share = ((int64_t)batch * max_len + h->num_cu - 1) / h->num_cu;
     int64_t c = round_up(share, mfa::kStep);
     if (c < kMinAutoSplit) c = kMinAutoSplit;
-    if (c > kMaxAutoSplit) c = kMaxAutoSplit;
+    if (c > max_auto) c = max_auto;
     if (c > round_up(max_len, mfa::kStep)) c = round_up(max_len, mfa::kStep);
     return (int32_t)c;
+}
+
+// The chunked split of a call with `rows` query-row sets: the chunk and the
+// number of head groups per (row set, chunk). In the FP8-MFMA mode the 64
+// heads may go to two workgroups of 32 when the doubled grid still fits on
+// the compute units at once: both read the same K/V rows (the second from
+// L2), and a sequence then needs half as many chunks, so fewer partials to
+// merge. With bf16 MFMAs each workgroup would widen every FP8 row itself,
+// and that doubled VALU work costs more than the merges it saves.
+static void plan_chunks(const mfa_ctx* h, int32_t rows, int32_t max_len, int32_t* chunk, int32_t* nh) {
+    *nh = 1;
+    *chunk = choose_split(h, rows, max_len);
+    if (h->cfg.attn_math != MFA_ATTN_FP8_MFMA || max_len <= 0) return;
+    // chunks up to the paged limit: with two workgroups per chunk, the
+    // longer chunk still leaves every compute unit one workgroup
+    const int32_t c2 = choose_split(h, 2 * rows, max_len, mfa::kMaxPagedChunkSteps * mfa::kStep);
+    const int64_t n2 = (max_len + c2 - 1) / c2;
+    if (2 * (int64_t)rows * n2 <= h->num_cu) {
+        *chunk = c2;
+        *nh = 2;
+    }
 }
 
 extern "C" {
@@ -207,7 +228,8 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     }
     constexpr int kBuffers = 8;
     void* p[kBuffers] = {};
-    const int64_t sizes[kBuffers] = {bytes_o,  bytes_lse, bytes_c,     bytes_chat, (int64_t)c.max_batch * 4,
+    const int64_t bytes_ctr = 2 * (int64_t)c.max_batch * 4;   // per (query row set, head half)
+    const int64_t sizes[kBuffers] = {bytes_o,  bytes_lse, bytes_c,     bytes_chat, bytes_ctr,
                                      bytes_kv, bytes_sumsq, bytes_qctr};
     for (int i = 0; i < kBuffers; i++) {
         e = hipMalloc(&p[i], (size_t)sizes[i]);
@@ -227,7 +249,7 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     h->kv_part = (float*)p[5];
     h->sumsq = (float*)p[6];
     h->qcounters = (int32_t*)p[7];
-    e = hipMemset(h->counters, 0, (size_t)c.max_batch * 4);
+    e = hipMemset(h->counters, 0, (size_t)bytes_ctr);
     if (e == hipSuccess) e = hipMemset(h->qcounters, 0, (size_t)bytes_qctr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -262,7 +284,18 @@ int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_split_tokens: not a live handle");
     if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;
     if (use_balanced(h, batch, max_seq_len, min_seq_len)) return 0;
-    return choose_split(h, batch, max_seq_len);
+    int32_t chunk, nh;
+    plan_chunks(h, batch, max_seq_len, &chunk, &nh);
+    return chunk;
+}
+
+int32_t mfa_head_groups(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len) {
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_head_groups: not a live handle");
+    if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;
+    if (use_balanced(h, batch, max_seq_len, min_seq_len)) return 1;
+    int32_t chunk, nh;
+    plan_chunks(h, batch, max_seq_len, &chunk, &nh);
+    return nh;
 }
 
 int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w, const void* w_qb,
@@ -379,21 +412,24 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
         a.n_chunk = 0;
         a.part_stride = h->max_chunks + 1;
         a.fuse_max = 1 << 30;   // the last piece of a sequence always merges
+        a.nh = 1;
         const int64_t bound = (int64_t)batch * ((max_len + mfa::kStep - 1) / mfa::kStep);
         int64_t g = h->num_cu;
         if (bound > g * mfa::kMaxPagedChunkSteps) g = round_up((bound + mfa::kMaxPagedChunkSteps - 1) / mfa::kMaxPagedChunkSteps, h->num_cu);
         workgroups = (int)g;
     } else {
         a.balanced = 0;
-        a.chunk = choose_split(h, rows, max_len);
+        plan_chunks(h, rows, max_len, &a.chunk, &a.nh);
         a.n_chunk = (max_len + a.chunk - 1) / a.chunk;
         if (a.n_chunk < 1) a.n_chunk = 1;
         if (a.n_chunk > h->max_chunks)
             return fail(MFA_ERR_INVALID, "%s: %d chunks exceed the workspace (%d)", fn, a.n_chunk, h->max_chunks);
         a.part_stride = a.n_chunk;
         a.fuse_max = a.n_chunk <= mfa::kFusedMaxChunks ? mfa::kFusedMaxChunks : 1;
-        // multi-token: groups of 8 work items times qtok tokens (see the kernel)
-        workgroups = qtok == 1 ? batch * a.n_chunk : round_up((int64_t)batch * a.n_chunk, 8) * qtok;
+        // several workgroups per (sequence, chunk) (tokens, head halves):
+        // groups of 8 work items times their number (see the kernel)
+        const int reps = qtok * a.nh;
+        workgroups = reps == 1 ? batch * a.n_chunk : round_up((int64_t)batch * a.n_chunk, 8) * reps;
     }
     const float log2e = 1.4426950408889634f;
     a.score_scale = h->cfg.softmax_scale * (fp8 ? kv->k_scale : 1.0f) * log2e;

@@ -216,37 +216,46 @@ void mfa_attn_split_kernel(const AttnArgs p) {
 }
 
 // FP8 caches: the same work split, eight waves in two roles (the body in
-// mfa_attn_ws.inc).
-template <bool PAGED, bool MTP, bool F8MMA>
+// mfa_attn_ws.inc). With several workgroups per (sequence, chunk) -- the t
+// query tokens of multi-token decode and, with HS, the two head halves --
+// those workgroups get block indices 8 apart inside a group of 8 times their
+// number, so that the round-robin dispatch puts them on one XCD at about the
+// same time and the K/V rows come from HBM once.
+template <bool PAGED, bool MTP, bool F8MMA, bool HS>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void mfa_attn_ws_split_kernel(const AttnArgs p) {
-    int b, c, kvb, L;
-    if constexpr (!MTP) {
+    int b, c, kvb, L, half = 0;
+    const int reps = p.qtok * p.nh;
+    if (reps == 1) {
         b = blockIdx.x / p.n_chunk;
         c = blockIdx.x - b * p.n_chunk;
         kvb = b;
         L = seq_len(p.kv, b);
     } else {
-        const int t = p.qtok;
-        const int grp = blockIdx.x / (8 * t);
-        const int r = blockIdx.x - grp * 8 * t;
+        const int grp = blockIdx.x / (8 * reps);
+        const int r = blockIdx.x - grp * 8 * reps;
         const int wi = grp * 8 + (r & 7);   // (sequence, chunk) work item
         if (wi >= p.batch * p.n_chunk) return;
         kvb = wi / p.n_chunk;
         c = wi - kvb * p.n_chunk;
-        const int j = r >> 3;
-        b = kvb * t + j;
-        L = max(0, seq_len(p.kv, kvb) - (t - 1 - j));
+        const int rep = r >> 3;
+        const int j = rep % p.qtok;         // query token
+        if constexpr (HS) half = rep / p.qtok;
+        b = kvb * p.qtok + j;
+        L = seq_len(p.kv, kvb);
+        if constexpr (MTP) L = max(0, L - (p.qtok - 1 - j));
     }
+    const int hb = 32 * half;
     const int t_begin = c * p.chunk;
 
     if (t_begin >= L) {
-        if (c == 0) {  // empty sequence: out = 0, lse = -inf
-            uint16_t* ob = p.out + (int64_t)b * kHeads * kHeadDim;
-            for (int i = threadIdx.x; i < kHeads * kHeadDim / 8; i += 512)
+        if (c == 0) {  // empty sequence: out = 0, lse = -inf for this workgroup's heads
+            constexpr int NHW = HS ? 32 : 64;
+            uint16_t* ob = p.out + ((int64_t)b * kHeads + hb) * kHeadDim;
+            for (int i = threadIdx.x; i < NHW * kHeadDim / 8; i += 512)
                 reinterpret_cast<u32x4*>(ob)[i] = u32x4{0, 0, 0, 0};
-            if (p.lse_out && threadIdx.x < kHeads)
-                p.lse_out[b * kHeads + threadIdx.x] = -__builtin_inff();
+            if (p.lse_out && threadIdx.x < NHW)
+                p.lse_out[b * kHeads + hb + threadIdx.x] = -__builtin_inff();
         }
         return;
     }
@@ -288,6 +297,8 @@ template <bool PAGED, bool F8MMA>
 __device__ __forceinline__ void attend_piece_ws(const AttnArgs& p, const int b, const int L, const int t_begin,
                                                 const int t_end, const int piece_k, const int nparts,
                                                 const int64_t part_base) {
+    constexpr bool HS = false;
+    const int hb = 0;
     const int kvb = b;
     const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
     const int last_s = nsteps - 1;
@@ -530,12 +541,16 @@ __global__ __launch_bounds__(256) void mfa_gather_kernel(const KvView kv, int b,
 
 hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l) {
     const dim3 grid(workgroups), block(256), block_ws(512);
+    const bool hs = a.nh == 2;
     if (a.fp8_mma) {   // FP8 cache only (checked by the caller)
         if (a.balanced)
             return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, true>, grid, block_ws, l, a)
                          : launch_kernel(mfa_attn_balanced_kernel<true, false, true>, grid, block_ws, l, a);
-        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true>, grid, block_ws, l, a)
-                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, true>, grid, block_ws, l, a);
+        if (hs)
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true, true>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, true>, grid, block_ws, l, a);
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true, false>, grid, block_ws, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, false>, grid, block_ws, l, a);
     }
     if (a.balanced) {
         if (fp8)
@@ -544,16 +559,23 @@ hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgr
         return paged ? launch_kernel(mfa_attn_balanced_kernel<false, true, false>, grid, block, l, a)
                      : launch_kernel(mfa_attn_balanced_kernel<false, false, false>, grid, block, l, a);
     }
-    if (a.qtok > 1) {
-        if (fp8)
-            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_ws_split_kernel<false, true, false>, grid, block_ws, l, a);
+    if (fp8) {
+        if (a.qtok > 1) {
+            if (hs)
+                return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, true>, grid, block_ws, l, a)
+                             : launch_kernel(mfa_attn_ws_split_kernel<false, true, false, true>, grid, block_ws, l, a);
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, false>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, true, false, false>, grid, block_ws, l, a);
+        }
+        if (hs)
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, true>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, true>, grid, block_ws, l, a);
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, false>, grid, block_ws, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, false>, grid, block_ws, l, a);
+    }
+    if (a.qtok > 1)
         return paged ? launch_kernel(mfa_attn_split_kernel<false, true, true, false>, grid, block, l, a)
                      : launch_kernel(mfa_attn_split_kernel<false, false, true, false>, grid, block, l, a);
-    }
-    if (fp8)
-        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false>, grid, block_ws, l, a)
-                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, false>, grid, block_ws, l, a);
     return paged ? launch_kernel(mfa_attn_split_kernel<false, true, false, false>, grid, block, l, a)
                  : launch_kernel(mfa_attn_split_kernel<false, false, false, false>, grid, block, l, a);
 }

@@ -148,3 +148,27 @@ def test_fp8_mma_full_size(cfg):
     el = np.abs(lse[idx] - lse_ref).max()
     _say(f"    row-rel err {err.max():.3e}  lse abs err {el:.3e}")
     assert err.max() <= TOL_F8 and el <= LSE_TOL_F8
+
+
+def test_head_split_policy():
+    """FP8-MFMA mode at the FP8 workload's size: the 64 heads go to two
+    workgroups per sequence (one chunk each, nothing to merge); with bf16
+    MFMAs they stay together and each sequence takes two chunks."""
+    m, hz = _mfa()
+    case = synth.config_case(3, batch=1)
+    dc = hz.to_device(case)
+    for math, groups in ((m.MFA_ATTN_FP8_MFMA, 2), (m.MFA_ATTN_BF16_MFMA, 1)):
+        h = hz.create_handle(dc, max_batch=128, attn_math=math)
+        try:
+            n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+            g = m.mfa_head_groups(h, 128, 4096, 4096)
+            split = m.mfa_split_tokens(h, 128, 4096, 4096)
+            _say(f"[head split] math={math} cu={n_cu} groups={g} split={split}")
+            if n_cu == 256:
+                assert g == groups
+                assert split == (4096 if groups == 2 else 2048)
+            assert g in (1, 2)
+            if g == 2:   # the doubled grid fits on the compute units at once
+                assert 2 * 128 * ((4096 + split - 1) // split) <= n_cu
+        finally:
+            m.mfa_destroy(h)
