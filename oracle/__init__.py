@@ -64,6 +64,9 @@ def _load():
         lib.oracle_attention.argtypes = [I, I, I, P, I, P, P, D, D, P, P, I, I, I64, D, I,
                                          P, P, I]
         lib.oracle_attention.restype = I
+        lib.oracle_attention_grouped.argtypes = [I, I, I, I, P, I, P, P, D, D, P, P, I, I, I64, D, I,
+                                                 P, P, I]
+        lib.oracle_attention_grouped.restype = I
         lib.oracle_weights.argtypes = [I, I, P, I, I, I, P, D, P, P, I, I, I64, D, P]
         lib.oracle_weights.restype = I
         lib.oracle_gather_kv.argtypes = [I, I, I, P, P, P, P, I, I, I64, P, P]
@@ -190,34 +193,43 @@ def qproj(x, w_qa, gamma, w_qb, eps: float = 1e-6, nthreads: int = 0, return_c: 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, *, kv_dtype: int,
               k_scale: float = 1.0, v_scale: float = 1.0, page_table=None, page_size: int = 64,
-              softmax_scale: float = 1.0 / 16.0, chunk: int = 0, nthreads: int = 0):
+              softmax_scale: float = 1.0 / 16.0, chunk: int = 0, nthreads: int = 0, kv_heads: int = 1):
     """q [B, H, D] fp64; k, v contiguous [B, S, D] or paged [P, page, D] as raw
-    bits (uint16 bf16 or uint8 E4M3). Returns (o [B, H, D], lse [B, H]) fp64."""
+    bits (uint16 bf16 or uint8 E4M3). With kv_heads = G > 1 (grouped-query
+    attention): k, v contiguous [B, G, S, D] or paged [P, G, page, D], query
+    head h reading KV head h // (H // G). Returns (o [B, H, D], lse [B, H])
+    fp64."""
     q = _c(q, np.float64)
     B, H, D = q.shape
+    G = int(kv_heads)
     raw = np.uint16 if kv_dtype == KV_BF16 else np.uint8
     k = _c(k, raw)
     v = _c(v, raw)
     L = _c(seq_lens, np.int32)
     assert L.shape == (B,)
+    if k.ndim == 4:   # grouped layout [., G, ., D] (G may be 1)
+        assert k.shape[1] == G, "grouped caches are [., G, ., D]"
+    else:
+        assert G == 1, "grouped caches are [., G, ., D]"
+    rows_axis = 2 if k.ndim == 4 else 1
     if page_table is not None:
         pt = _c(page_table, np.int32)
         pt_stride = pt.shape[1]
         kv_stride = 0
-        page_size = k.shape[1]
+        page_size = k.shape[rows_axis]
     else:
         pt = None
         pt_stride = 0
-        kv_stride = k.shape[1]
+        kv_stride = k.shape[rows_axis]
     assert k.shape[-1] == D and v.shape == k.shape
     o = np.empty((B, H, D), dtype=np.float64)
     lse = np.empty((B, H), dtype=np.float64)
-    rc = _load().oracle_attention(B, H, D, _ptr(q), kv_dtype, _ptr(k), _ptr(v), float(k_scale),
-                                  float(v_scale), _ptr(L), _ptr(pt), pt_stride, page_size,
-                                  kv_stride, float(softmax_scale), int(chunk), _ptr(o), _ptr(lse),
-                                  nthreads)
+    rc = _load().oracle_attention_grouped(B, H, G, D, _ptr(q), kv_dtype, _ptr(k), _ptr(v), float(k_scale),
+                                          float(v_scale), _ptr(L), _ptr(pt), pt_stride, page_size,
+                                          kv_stride, float(softmax_scale), int(chunk), _ptr(o), _ptr(lse),
+                                          nthreads)
     if rc:
-        raise RuntimeError(f"oracle_attention failed: {rc}")
+        raise RuntimeError(f"oracle_attention_grouped failed: {rc}")
     return o, lse
 
 

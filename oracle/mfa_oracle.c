@@ -30,7 +30,10 @@
  *     output), merged by the log-sum-exp identity;
  *   - the new token's K and V rows are x . W_k and x . W_v (hidden -> 256),
  *     rounded to float, divided by the tensor's scale for FP8, encoded by
- *     round-to-nearest-even (E4M3 saturating at +-448) and written at row L_b.
+ *     round-to-nearest-even (E4M3 saturating at +-448) and written at row L_b;
+ *   - for the head-sharing comparison, grouped-query attention (GQA, cited by
+ *     title on the DeepSeek-V4 page): G K/V heads, query head h reading head
+ *     h / (H / G), caches [B][G][S][D] or pools [P][G][page][D].
  *
  * Every floating-point step runs in IEEE double. Inputs in bf16 / E4M3 are
  * decoded exactly (both formats are subsets of double).
@@ -45,7 +48,9 @@
  * against torch and against exact midpoints between neighbouring codes (ties
  * to even), saturation, the K/V projection against numpy dgemm and decimal
  * brute force, and the append touching exactly row L_b (paged and contiguous
- * agreeing).
+ * agreeing); grouped attention against torch's grouped SDPA (enable_gqa),
+ * as G independent single-head problems, paged equal to contiguous, and a
+ * decimal brute force.
  */
 #include <math.h>
 #include <stdint.h>
@@ -200,15 +205,20 @@ typedef struct {
     int page_size;
     int64_t kv_stride;         /* contiguous: token slots per sequence */
     int D;
+    int G;                     /* KV heads (1: one K and one V head shared by all query heads) */
+    int g;                     /* the KV head this view reads */
 } kv_view;
 
-/* Row index (in units of D elements) of token t of sequence b. */
+/* Row index (in units of D elements) of token t of sequence b in KV head
+ * kv->g. Contiguous: K/V [B][G][kv_stride][D]; paged: pools
+ * [P][G][page_size][D], page_table[b][t / page_size] naming the page. With
+ * G = 1 these are [B][kv_stride][D] and [P][page_size][D]. */
 static int64_t kv_row(const kv_view* kv, int b, int t) {
     if (kv->page_table) {
         int32_t page = kv->page_table[(size_t)b * kv->pt_stride + t / kv->page_size];
-        return (int64_t)page * kv->page_size + t % kv->page_size;
+        return ((int64_t)page * kv->G + kv->g) * kv->page_size + t % kv->page_size;
     }
-    return (int64_t)b * kv->kv_stride + t;
+    return ((int64_t)b * kv->G + kv->g) * kv->kv_stride + t;
 }
 
 static double kv_value(const kv_view* kv, const void* base, double scale, int64_t row, int d) {
@@ -279,25 +289,32 @@ static int check_args(int B, int H, int D, const int32_t* seq_lens, int page_siz
 }
 
 /* q [B][H][D] fp64. Outputs o [B][H][D], lse [B][H] (lse may be NULL).
+ * G KV heads (grouped-query attention, "GQA: Training Generalized
+ * Multi-Query Transformer Models from Multi-Head Checkpoints", named on the
+ * DeepSeek-V4 card's references): query head h reads KV head
+ * h / (H / G), consecutive query heads sharing one; G = 1 is MFA's single
+ * shared K/V head, G = H is multi-head attention. G must divide H.
  * chunk <= 0: one softmax over all L_b tokens.
  * chunk > 0: split-K. Each chunk [c*chunk, min(L_b, (c+1)*chunk)) yields
  * lse_c and the chunk-normalised output o_c; then
  * LSE = M + log sum_c exp(lse_c - M) with M = max_c lse_c and
  * o = sum_c exp(lse_c - LSE) * o_c. */
-int oracle_attention(int B, int H, int D, const double* q, int kv_dtype,
-                     const void* k, const void* v, double k_scale, double v_scale,
-                     const int32_t* seq_lens, const int32_t* page_table, int pt_stride,
-                     int page_size, int64_t kv_stride, double softmax_scale, int chunk,
-                     double* o, double* lse, int nthreads) {
+int oracle_attention_grouped(int B, int H, int G, int D, const double* q, int kv_dtype,
+                             const void* k, const void* v, double k_scale, double v_scale,
+                             const int32_t* seq_lens, const int32_t* page_table, int pt_stride,
+                             int page_size, int64_t kv_stride, double softmax_scale, int chunk,
+                             double* o, double* lse, int nthreads) {
     int rc = check_args(B, H, D, seq_lens, page_size, page_table, pt_stride, kv_stride);
     if (rc)
         return rc;
+    if (G <= 0 || H % G != 0)
+        return -1;
     if (kv_dtype != OR_BF16 && kv_dtype != OR_FP8_E4M3)
         return -2;
     e4m3_table_init();
     set_threads(nthreads);
-    kv_view kv = {kv_dtype, k, v, k_scale, v_scale, page_table, pt_stride, page_size,
-                  kv_stride, D};
+    const kv_view kv0 = {kv_dtype, k, v, k_scale, v_scale, page_table, pt_stride, page_size,
+                         kv_stride, D, G, 0};
     int maxL = 0;
     for (int b = 0; b < B; b++)
         if (seq_lens[b] > maxL)
@@ -315,6 +332,8 @@ int oracle_attention(int B, int H, int D, const double* q, int kv_dtype,
             if (failed)
                 continue;
             int b = (int)(bh / H);
+            kv_view kv = kv0;
+            kv.g = (int)(bh % H) / (H / G);   /* the KV head of query head h */
             const double* qv = q + (size_t)bh * D;
             double* ov = o + (size_t)bh * D;
             double l_out;
@@ -365,6 +384,17 @@ int oracle_attention(int B, int H, int D, const double* q, int kv_dtype,
     return failed ? -3 : 0;
 }
 
+/* One K and one V head shared by all H query heads (MFA's attention). */
+int oracle_attention(int B, int H, int D, const double* q, int kv_dtype,
+                     const void* k, const void* v, double k_scale, double v_scale,
+                     const int32_t* seq_lens, const int32_t* page_table, int pt_stride,
+                     int page_size, int64_t kv_stride, double softmax_scale, int chunk,
+                     double* o, double* lse, int nthreads) {
+    return oracle_attention_grouped(B, H, 1, D, q, kv_dtype, k, v, k_scale, v_scale, seq_lens,
+                                    page_table, pt_stride, page_size, kv_stride, softmax_scale,
+                                    chunk, o, lse, nthreads);
+}
+
 /* Softmax weights of one (b, h) over all L_b tokens, in token order:
  * w[t] = exp(s_t - M) / sum_u exp(s_u - M). For the sum-to-one pin. */
 int oracle_weights(int H, int D, const double* q, int b, int h, int kv_dtype,
@@ -373,7 +403,7 @@ int oracle_weights(int H, int D, const double* q, int b, int h, int kv_dtype,
                    double softmax_scale, double* w) {
     (void)H;
     e4m3_table_init();
-    kv_view kv = {kv_dtype, k, k, k_scale, 1.0, page_table, pt_stride, page_size, kv_stride, D};
+    kv_view kv = {kv_dtype, k, k, k_scale, 1.0, page_table, pt_stride, page_size, kv_stride, D, 1, 0};
     int L = seq_lens[b];
     if (L <= 0)
         return 0;
@@ -397,7 +427,7 @@ int oracle_weights(int H, int D, const double* q, int b, int h, int kv_dtype,
 int oracle_gather_kv(int b, int D, int elem_bytes, const void* k, const void* v,
                      const int32_t* seq_lens, const int32_t* page_table, int pt_stride,
                      int page_size, int64_t kv_stride, void* k_dst, void* v_dst) {
-    kv_view kv = {0, k, v, 1.0, 1.0, page_table, pt_stride, page_size, kv_stride, D};
+    kv_view kv = {0, k, v, 1.0, 1.0, page_table, pt_stride, page_size, kv_stride, D, 1, 0};
     int L = seq_lens[b];
     size_t rb = (size_t)D * elem_bytes;
     for (int t = 0; t < L; t++) {

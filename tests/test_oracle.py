@@ -538,3 +538,98 @@ def test_mtp_token_with_no_rows():
                                   v_scale=case.v_scale)
     assert np.all(o[0, :2] == 0) and np.all(np.isneginf(lse[0, :2]))
     assert np.all(np.isfinite(lse[0, 2:]))
+
+
+# ------------------------------------------------------- grouped KV heads (GQA)
+def _gqa_inputs(B, G, L, kv, seed, H=16, D=8, paged=False):
+    """Small grouped caches: q [B, H, D] fp64, K/V raw [B, G, S, D] (or paged
+    pools [P, G, 64, D] with a permuted page table)."""
+    rng = np.random.default_rng(seed)
+    q = _torch_decode_bf16(synth.bf16_bits(rng.standard_normal((B, H, D)).astype(np.float32)))
+    S = max(L)
+    Kf = rng.standard_normal((B, G, S, D)).astype(np.float32)
+    Vf = rng.standard_normal((B, G, S, D)).astype(np.float32)
+    if kv == "bf16":
+        K, V, ks, vs, code = synth.bf16_bits(Kf), synth.bf16_bits(Vf), 1.0, 1.0, BF16
+        dec = _torch_decode_bf16
+    else:
+        K, V, ks, vs, code = synth.e4m3_codes(Kf), synth.e4m3_codes(Vf), 0.5, 0.75, FP8
+        dec = _torch_decode_e4m3
+    Kd, Vd = dec(K) * ks, dec(V) * vs
+    return q, K, V, Kd, Vd, ks, vs, code
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("G", [1, 2, 4, 16])
+def test_gqa_matches_torch_sdpa_enable_gqa(kv, G):
+    """Grouped-query attention against torch's own grouped SDPA (float64,
+    CPU, enable_gqa: query head h uses KV head h // (H // G)); G = H is
+    multi-head attention, G = 1 MFA's single shared head."""
+    L = [5, 33, 64]
+    q, K, V, Kd, Vd, ks, vs, code = _gqa_inputs(3, G, L, kv, seed=300 + G)
+    o, lse = oracle.attention(q, K, V, np.array(L, np.int32), kv_dtype=code, k_scale=ks, v_scale=vs,
+                              softmax_scale=0.3, kv_heads=G)
+    for b, n in enumerate(L):
+        qt = torch.from_numpy(q[b])[None, :, None, :]                 # [1, H, 1, D]
+        kt = torch.from_numpy(Kd[b, :, :n])[None]                      # [1, G, n, D]
+        vt = torch.from_numpy(Vd[b, :, :n])[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.3, enable_gqa=True)
+        assert _rel(o[b], ref[0, :, 0].numpy()) < 1e-12
+        grp = np.arange(q.shape[1]) // (q.shape[1] // G)
+        s = np.einsum("hd,htd->ht", q[b], Kd[b, grp, :n]) * 0.3
+        assert np.max(np.abs(lse[b] - torch.logsumexp(torch.from_numpy(s), dim=1).numpy())) < 1e-12
+
+
+def test_gqa_is_independent_mqa_per_group():
+    """Each group is MFA's single-head attention of its own query heads
+    against its own K/V head: the grouped result equals G separate calls."""
+    G, H = 4, 16
+    L = [17, 40]
+    q, K, V, Kd, Vd, ks, vs, code = _gqa_inputs(2, G, L, "fp8", seed=310, H=H)
+    o, lse = oracle.attention(q, K, V, np.array(L, np.int32), kv_dtype=code, k_scale=ks, v_scale=vs,
+                              softmax_scale=0.25, kv_heads=G)
+    hg = H // G
+    for g in range(G):
+        og, lg = oracle.attention(np.ascontiguousarray(q[:, g * hg:(g + 1) * hg]), np.ascontiguousarray(K[:, g]),
+                                  np.ascontiguousarray(V[:, g]), np.array(L, np.int32), kv_dtype=code,
+                                  k_scale=ks, v_scale=vs, softmax_scale=0.25)
+        assert np.array_equal(og, o[:, g * hg:(g + 1) * hg]) and np.array_equal(lg, lse[:, g * hg:(g + 1) * hg])
+
+
+def test_gqa_paged_equals_contiguous_bitwise():
+    """Paged grouped pools [P, G, 64, D] through a permuted page table give
+    the contiguous grouped result bit for bit."""
+    G, L = 2, [70, 129, 1]
+    q, K, V, _, _, ks, vs, code = _gqa_inputs(3, G, L, "fp8", seed=320, H=8)
+    npg = [(n + 63) // 64 for n in L]
+    P = sum(npg)
+    perm = np.random.default_rng(321).permutation(P).astype(np.int32)
+    pt = np.zeros((3, max(npg)), np.int32)
+    Kp = np.zeros((P, G, 64, K.shape[-1]), np.uint8)
+    Vp = np.zeros_like(Kp)
+    i = 0
+    S = K.shape[2]
+    for b, n in enumerate(L):
+        for j in range(npg[b]):
+            page = perm[i]
+            i += 1
+            pt[b, j] = page
+            rows = min(64, S - 64 * j)
+            Kp[page, :, :rows] = K[b, :, 64 * j:64 * j + rows]
+            Vp[page, :, :rows] = V[b, :, 64 * j:64 * j + rows]
+    oc, lc = oracle.attention(q, K, V, np.array(L, np.int32), kv_dtype=code, k_scale=ks, v_scale=vs, kv_heads=G)
+    op, lp = oracle.attention(q, Kp, Vp, np.array(L, np.int32), kv_dtype=code, k_scale=ks, v_scale=vs,
+                              page_table=pt, kv_heads=G)
+    assert np.array_equal(oc, op) and np.array_equal(lc, lp)
+
+
+def test_gqa_tiny_brute_force_decimal():
+    """50-digit decimal softmax per query head against its group's K/V."""
+    G, H, D, L = 2, 4, 3, [6]
+    q, K, V, Kd, Vd, ks, vs, code = _gqa_inputs(1, G, L, "bf16", seed=330, H=H, D=D)
+    o, lse = oracle.attention(q, K, V, np.array(L, np.int32), kv_dtype=code, softmax_scale=0.6, kv_heads=G)
+    for h in range(H):
+        g = h // (H // G)
+        ro, rl = _decimal_attention(q[0, h:h + 1], Kd[0, g, :6], Vd[0, g, :6], 0.6)
+        assert np.max(np.abs(o[0, h] - ro[0])) <= 1e-14 * max(1.0, np.max(np.abs(ro)))
+        assert abs(lse[0, h] - rl[0]) <= 1e-14 * max(1.0, abs(rl[0]))
