@@ -39,9 +39,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MFA decode tokens/s per layer (1 GPU) + achieved HBM GB/s vs roofline"
 HBM_PEAK_GBPS = 8000.0
 WORKLOADS = {"tiny": 1, "full_layer": 2, "fp8_contig": 3, "paged_ragged": 4, "long_splitk": 5,
-             "decode_step": 2, "paged_append": 4, "fp8_mtp2": 3, "fp8_mtp4": 3}
+             "decode_step": 2, "paged_append": 4, "fp8_mtp2": 3, "fp8_mtp4": 3, "fp8_gqa2": 3, "fp8_gqa4": 3}
 APPEND = ("decode_step", "paged_append")
 MTP = {"fp8_mtp2": 2, "fp8_mtp4": 4}   # query tokens per sequence
+GQA = {"fp8_gqa2": 2, "fp8_gqa4": 4}   # K/V heads (head-sharing comparison)
 DESCRIPTION = {
     "tiny": "B=1, L=256, bf16 KV, contiguous, decode only",
     "full_layer": "B=32, L=4096, bf16 KV, contiguous, Q projection 7168->2048 (RMSNorm)->64x256 + decode",
@@ -54,6 +55,8 @@ DESCRIPTION = {
                     "row L_b) + decode over L_b+1",
     "fp8_mtp2": "B=128, L=4096, FP8-E4M3 KV, contiguous, 2 query tokens per sequence (multi-token decode)",
     "fp8_mtp4": "B=128, L=4096, FP8-E4M3 KV, contiguous, 4 query tokens per sequence (multi-token decode)",
+    "fp8_gqa2": "B=128, L=4096, FP8-E4M3 KV, contiguous, 64 query heads on 2 K/V heads (grouped-query comparison)",
+    "fp8_gqa4": "B=128, L=4096, FP8-E4M3 KV, contiguous, 64 query heads on 4 K/V heads (grouped-query comparison)",
 }
 # sources that decide the attention kernel's memory traffic (kernel, launch
 # shape, split and merge policy); the stored HBM counters hold for this hash
@@ -87,8 +90,8 @@ def attn_source_sha() -> str:
 
 def algorithmic_bytes(case, attention_writes_out: bool, append: bool = False, qtok: int = 1):
     """(attention-kernel bytes, whole-step bytes) the method must move.
-    Attention: every cached K and V row t < L_b (512 B per token with FP8,
-    1024 B with bf16; t <= L_b after an append), Q (32 KB per sequence), the
+    Attention: every cached K and V row t < L_b (512 B per token and K/V
+    head with FP8, 1024 B with bf16; t <= L_b after an append), Q (32 KB per sequence), the
     lengths and (paged) the page-table entries it reads, and the bf16 output
     (32 KB per sequence) when the attention kernel writes it (no separate
     merge launch). Step: all of that plus the output; with the Q projection,
@@ -99,7 +102,7 @@ def algorithmic_bytes(case, attention_writes_out: bool, append: bool = False, qt
     B = case.batch
     L = case.seq_lens.astype(np.int64) + (1 if append else 0)
     elem = 1 if case.kv_dtype == "fp8" else 2
-    kv = int(L.sum()) * 2 * 256 * elem
+    kv = int(L.sum()) * 2 * 256 * elem * getattr(case, "kv_heads", 1)
     q = B * qtok * 64 * 256 * 2
     o = B * qtok * 64 * 256 * 2
     meta = B * 4
@@ -235,7 +238,7 @@ def main():
     t0 = time.perf_counter()
     append = wl in APPEND
     qtok = MTP.get(wl, 1)
-    case = synth.config_case(WORKLOADS[wl], append=append)
+    case = synth.gqa_case(GQA[wl]) if wl in GQA else synth.config_case(WORKLOADS[wl], append=append)
     if qtok > 1:
         case.q = synth.mtp_queries(case.batch, qtok, case.seed)
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s")
@@ -349,7 +352,8 @@ def main():
                    "query_tokens": qtok,
                    "attn_math": "fp8 MFMA (quantised Q and P)" if args.attn_math == "fp8" else "bf16 MFMA",
                    "work_split": ("balanced ranges of steps" if split == 0 else f"chunks of {split} tokens")
-                   + (", heads in two workgroups of 32" if head_groups == 2 else ""),
+                   + (f", heads in {head_groups} workgroups of {64 // head_groups}" if head_groups > 1 else ""),
+                   "kv_heads": getattr(case, "kv_heads", 1),
                    "input_sets_rotated": nrot, "mall": "cold" if cold else "warm"},
         "step_hbm_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": attn_kernel_name(split, case.kv_dtype == "fp8"),

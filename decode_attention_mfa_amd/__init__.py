@@ -41,7 +41,8 @@ class mfa_config(ctypes.Structure):
                 ("kv_dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("max_batch", ctypes.c_int32), ("max_context", ctypes.c_int32),
                 ("split_tokens", ctypes.c_int32), ("rms_eps", ctypes.c_float),
-                ("softmax_scale", ctypes.c_float), ("attn_math", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("attn_math", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32)]
 
 
 class mfa_kv(ctypes.Structure):
@@ -125,25 +126,26 @@ def mfa_last_error() -> str:
 
 def make_config(*, hidden=7168, q_rank=2048, num_heads=64, head_dim=256, kv_dtype=MFA_DTYPE_BF16,
                 page_size=0, max_batch=1, max_context=4096, split_tokens=0, rms_eps=1e-6,
-                softmax_scale=1.0 / 16.0, attn_math=MFA_ATTN_BF16_MFMA) -> mfa_config:
+                softmax_scale=1.0 / 16.0, attn_math=MFA_ATTN_BF16_MFMA, kv_heads=1) -> mfa_config:
     if isinstance(kv_dtype, str):
         kv_dtype = MFA_DTYPE_FP8_E4M3 if kv_dtype == "fp8" else MFA_DTYPE_BF16
     return mfa_config(hidden, q_rank, num_heads, head_dim, kv_dtype, page_size, max_batch,
-                      max_context, split_tokens, rms_eps, softmax_scale, attn_math)
+                      max_context, split_tokens, rms_eps, softmax_scale, attn_math, kv_heads)
 
 
 def make_kv(k, v, seq_lens, *, page_table=None, k_scale=1.0, v_scale=1.0, kv_stride=0,
             pt_stride=0, num_pages=0, max_seq_len=0, min_seq_len=0) -> mfa_kv:
     """Describe a KV cache. For torch tensors the strides default from the
-    shapes: contiguous k [B, S, 256] -> kv_stride S; paged k [P, 64, 256] ->
-    num_pages P; page_table [B, n] -> pt_stride n."""
+    shapes: contiguous k [B, S, 256] (or grouped [B, G, S, 256]) -> kv_stride
+    S; paged k [P, 64, 256] (or [P, G, 64, 256]) -> num_pages P; page_table
+    [B, n] -> pt_stride n."""
     if page_table is not None:
         if not pt_stride and hasattr(page_table, "shape"):
             pt_stride = int(page_table.shape[1])
         if not num_pages and hasattr(k, "shape"):
             num_pages = int(k.shape[0])
     elif not kv_stride and hasattr(k, "shape"):
-        kv_stride = int(k.shape[1])
+        kv_stride = int(k.shape[-2])
     return mfa_kv(_ptr(k), _ptr(v), k_scale, v_scale, _ptr(seq_lens), _ptr(page_table),
                   pt_stride, num_pages, kv_stride, max_seq_len, min_seq_len)
 

@@ -111,6 +111,7 @@ static int32_t kv_ksplit(int32_t hidden, int32_t batch) {
 // chunks are already balanced and need no length scan. Smaller batches of
 // long sequences keep per-sequence chunks and the separate merge kernel.
 static bool use_balanced(const mfa_ctx* h, int32_t batch, int32_t max_len, int32_t min_len) {
+    if (h->cfg.kv_heads > 1) return false;   // grouped caches: chunks, one workgroup per K/V head
     if (h->cfg.split_tokens == MFA_SPLIT_BALANCED) return true;
     if (h->cfg.split_tokens != 0 || 2 * batch < h->num_cu) return false;
     const bool uniform = min_len > 0 && (min_len + mfa::kStep - 1) / mfa::kStep == (max_len + mfa::kStep - 1) / mfa::kStep;
@@ -137,6 +138,11 @@ static int32_t choose_split(const mfa_ctx* h, int32_t batch, int32_t max_len, in
 // merge. With bf16 MFMAs each workgroup would widen every FP8 row itself,
 // and that doubled VALU work costs more than the merges it saves.
 static void plan_chunks(const mfa_ctx* h, int32_t rows, int32_t max_len, int32_t* chunk, int32_t* nh) {
+    if (h->cfg.kv_heads > 1) {   // grouped caches: one workgroup per (row set, chunk, K/V head)
+        *nh = h->cfg.kv_heads;
+        *chunk = choose_split(h, *nh * rows, max_len, mfa::kMaxPagedChunkSteps * mfa::kStep);
+        return;
+    }
     *nh = 1;
     *chunk = choose_split(h, rows, max_len);
     if (h->cfg.attn_math != MFA_ATTN_FP8_MFMA || max_len <= 0) return;
@@ -169,7 +175,7 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     g_last_error[0] = 0;
     if (!cfg || !out) return fail(MFA_ERR_INVALID, "mfa_create: null cfg or out");
     *out = nullptr;
-    const mfa_config c = *cfg;
+    mfa_config c = *cfg;
     if (c.num_heads != mfa::kHeads || c.head_dim != mfa::kHeadDim)
         return fail(MFA_ERR_UNSUPPORTED, "mfa_create: only 64 heads x 256 are supported (got %d x %d)",
                     c.num_heads, c.head_dim);
@@ -200,6 +206,13 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
         return fail(MFA_ERR_INVALID, "mfa_create: bad attn_math %d", c.attn_math);
     if (c.attn_math == MFA_ATTN_FP8_MFMA && c.kv_dtype != MFA_DTYPE_FP8_E4M3)
         return fail(MFA_ERR_UNSUPPORTED, "mfa_create: attn_math FP8_MFMA needs an FP8 cache");
+    if (c.kv_heads == 0) c.kv_heads = 1;
+    if (c.kv_heads != 1 && c.kv_heads != 2 && c.kv_heads != 4)
+        return fail(MFA_ERR_INVALID, "mfa_create: kv_heads must be 1, 2 or 4 (got %d)", c.kv_heads);
+    if (c.kv_heads > 1 && (c.kv_dtype != MFA_DTYPE_FP8_E4M3 || c.attn_math != MFA_ATTN_BF16_MFMA ||
+                           c.split_tokens == MFA_SPLIT_BALANCED))
+        return fail(MFA_ERR_UNSUPPORTED,
+                    "mfa_create: kv_heads > 1 needs an FP8 cache, MFA_ATTN_BF16_MFMA and chunked splits");
 
     const int min_chunk = c.split_tokens > 0 ? c.split_tokens : kMinAutoSplit;
     const int64_t max_chunks = ((int64_t)c.max_context + min_chunk - 1) / min_chunk;
@@ -228,7 +241,7 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     }
     constexpr int kBuffers = 8;
     void* p[kBuffers] = {};
-    const int64_t bytes_ctr = 2 * (int64_t)c.max_batch * 4;   // per (query row set, head half)
+    const int64_t bytes_ctr = 4 * (int64_t)c.max_batch * 4;   // per (query row set, head group)
     const int64_t sizes[kBuffers] = {bytes_o,  bytes_lse, bytes_c,     bytes_chat, bytes_ctr,
                                      bytes_kv, bytes_sumsq, bytes_qctr};
     for (int i = 0; i < kBuffers; i++) {
@@ -372,6 +385,7 @@ static mfa::KvView make_view(const mfa_ctx* h, const mfa_kv* kv, int32_t max_len
     v.pt_stride = kv->pt_stride;
     v.row_bytes = mfa::kHeadDim * (h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3 ? 1 : 2);
     v.max_len = max_len;
+    v.groups = h->cfg.kv_heads;
     return v;
 }
 
@@ -387,6 +401,8 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
     if (rc) return rc;
     if (qtok > 1 && h->cfg.attn_math == MFA_ATTN_FP8_MFMA)
         return fail(MFA_ERR_UNSUPPORTED, "%s: multi-token decode runs with bf16 MFMAs only", fn);
+    if (qtok > 1 && h->cfg.kv_heads > 1)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: multi-token decode needs kv_heads 1", fn);
     const int32_t rows = batch * qtok;   // query-row sets (one per sequence and token)
     if (rows > h->cfg.max_batch)
         return fail(MFA_ERR_INVALID, "%s: batch %d x num_tokens %d exceeds max_batch %d", fn, batch, qtok,
@@ -413,6 +429,7 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
         a.part_stride = h->max_chunks + 1;
         a.fuse_max = 1 << 30;   // the last piece of a sequence always merges
         a.nh = 1;
+        a.kv_groups = 1;
         const int64_t bound = (int64_t)batch * ((max_len + mfa::kStep - 1) / mfa::kStep);
         int64_t g = h->num_cu;
         if (bound > g * mfa::kMaxPagedChunkSteps) g = round_up((bound + mfa::kMaxPagedChunkSteps - 1) / mfa::kMaxPagedChunkSteps, h->num_cu);
@@ -420,6 +437,7 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
     } else {
         a.balanced = 0;
         plan_chunks(h, rows, max_len, &a.chunk, &a.nh);
+        a.kv_groups = h->cfg.kv_heads;
         a.n_chunk = (max_len + a.chunk - 1) / a.chunk;
         if (a.n_chunk < 1) a.n_chunk = 1;
         if (a.n_chunk > h->max_chunks)
@@ -460,6 +478,7 @@ int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v,
                   int32_t batch, void* hip_stream) {
     g_last_error[0] = 0;
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_kv_append: not a live handle");
+    if (h->cfg.kv_heads > 1) return fail(MFA_ERR_UNSUPPORTED, "mfa_kv_append: needs kv_heads 1");
     if (!x || !w_k || !w_v) return fail(MFA_ERR_INVALID, "mfa_kv_append: null x, w_k or w_v");
     int32_t max_len = 0;
     int rc = check_kv(h, kv, batch, "mfa_kv_append", &max_len);
@@ -496,6 +515,7 @@ int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, 
                         void* hip_stream) {
     g_last_error[0] = 0;
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_debug_gather_kv: not a live handle");
+    if (h->cfg.kv_heads > 1) return fail(MFA_ERR_UNSUPPORTED, "mfa_debug_gather_kv: needs kv_heads 1");
     if (!k_dst || !v_dst) return fail(MFA_ERR_INVALID, "mfa_debug_gather_kv: null destination");
     int32_t max_len = 0;
     int rc = check_kv(h, kv, h->cfg.max_batch, "mfa_debug_gather_kv", &max_len);

@@ -130,6 +130,18 @@ __device__ __forceinline__ void coherent_load_b128x8(f32x4* v, const f32x4* src,
         : "memory");
 }
 
+__device__ __forceinline__ void coherent_load_b128x4(f32x4* v, const f32x4* src, int stride) {
+    asm volatile(
+        "global_load_dwordx4 %0, %4, off sc1\n\t"
+        "global_load_dwordx4 %1, %5, off sc1\n\t"
+        "global_load_dwordx4 %2, %6, off sc1\n\t"
+        "global_load_dwordx4 %3, %7, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(src), "v"(src + stride), "v"(src + 2 * stride), "v"(src + 3 * stride)
+        : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 // The "memory" clobber keeps the compiler from moving LDS reads of the
 // DMA-filled ring above the wait.
@@ -217,14 +229,14 @@ void mfa_attn_split_kernel(const AttnArgs p) {
 
 // FP8 caches: the same work split, eight waves in two roles (the body in
 // mfa_attn_ws.inc). With several workgroups per (sequence, chunk) -- the t
-// query tokens of multi-token decode and, with HS, the two head halves --
+// query tokens of multi-token decode, or p.nh groups of 16 * NHT heads --
 // those workgroups get block indices 8 apart inside a group of 8 times their
 // number, so that the round-robin dispatch puts them on one XCD at about the
-// same time and the K/V rows come from HBM once.
-template <bool PAGED, bool MTP, bool F8MMA, bool HS>
+// same time (their shared K/V rows then come from HBM once).
+template <bool PAGED, bool MTP, bool F8MMA, int NHT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void mfa_attn_ws_split_kernel(const AttnArgs p) {
-    int b, c, kvb, L, half = 0;
+    int b, c, kvb, L, part = 0;
     const int reps = p.qtok * p.nh;
     if (reps == 1) {
         b = blockIdx.x / p.n_chunk;
@@ -240,17 +252,18 @@ void mfa_attn_ws_split_kernel(const AttnArgs p) {
         c = wi - kvb * p.n_chunk;
         const int rep = r >> 3;
         const int j = rep % p.qtok;         // query token
-        if constexpr (HS) half = rep / p.qtok;
+        if constexpr (NHT < 4) part = rep / p.qtok;
         b = kvb * p.qtok + j;
         L = seq_len(p.kv, kvb);
         if constexpr (MTP) L = max(0, L - (p.qtok - 1 - j));
     }
-    const int hb = 32 * half;
+    constexpr int NHW = 16 * NHT;           // heads of this workgroup
+    const int hb = NHW * part;
+    const int kvg = p.kv_groups > 1 ? part : 0;
     const int t_begin = c * p.chunk;
 
     if (t_begin >= L) {
         if (c == 0) {  // empty sequence: out = 0, lse = -inf for this workgroup's heads
-            constexpr int NHW = HS ? 32 : 64;
             uint16_t* ob = p.out + ((int64_t)b * kHeads + hb) * kHeadDim;
             for (int i = threadIdx.x; i < NHW * kHeadDim / 8; i += 512)
                 reinterpret_cast<u32x4*>(ob)[i] = u32x4{0, 0, 0, 0};
@@ -297,8 +310,8 @@ template <bool PAGED, bool F8MMA>
 __device__ __forceinline__ void attend_piece_ws(const AttnArgs& p, const int b, const int L, const int t_begin,
                                                 const int t_end, const int piece_k, const int nparts,
                                                 const int64_t part_base) {
-    constexpr bool HS = false;
-    const int hb = 0;
+    constexpr int NHT = 4;
+    const int hb = 0, kvg = 0;
     const int kvb = b;
     const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
     const int last_s = nsteps - 1;
@@ -541,16 +554,15 @@ __global__ __launch_bounds__(256) void mfa_gather_kernel(const KvView kv, int b,
 
 hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l) {
     const dim3 grid(workgroups), block(256), block_ws(512);
-    const bool hs = a.nh == 2;
     if (a.fp8_mma) {   // FP8 cache only (checked by the caller)
         if (a.balanced)
             return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, true>, grid, block_ws, l, a)
                          : launch_kernel(mfa_attn_balanced_kernel<true, false, true>, grid, block_ws, l, a);
-        if (hs)
-            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true, true>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, true>, grid, block_ws, l, a);
-        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true, false>, grid, block_ws, l, a)
-                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, false>, grid, block_ws, l, a);
+        if (a.nh == 2)
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true, 2>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, 2>, grid, block_ws, l, a);
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true, 4>, grid, block_ws, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, 4>, grid, block_ws, l, a);
     }
     if (a.balanced) {
         if (fp8)
@@ -560,18 +572,17 @@ hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgr
                      : launch_kernel(mfa_attn_balanced_kernel<false, false, false>, grid, block, l, a);
     }
     if (fp8) {
-        if (a.qtok > 1) {
-            if (hs)
-                return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, true>, grid, block_ws, l, a)
-                             : launch_kernel(mfa_attn_ws_split_kernel<false, true, false, true>, grid, block_ws, l, a);
-            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, false>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_ws_split_kernel<false, true, false, false>, grid, block_ws, l, a);
-        }
-        if (hs)
-            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, true>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, true>, grid, block_ws, l, a);
-        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, false>, grid, block_ws, l, a)
-                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, false>, grid, block_ws, l, a);
+        if (a.qtok > 1)   // bf16 MFMAs, all 64 heads per workgroup (checked by the caller)
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, 4>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, true, false, 4>, grid, block_ws, l, a);
+        if (a.nh == 4)    // grouped-query caches with four K/V heads
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, 1>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, 1>, grid, block_ws, l, a);
+        if (a.nh == 2)
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, 2>, grid, block_ws, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, 2>, grid, block_ws, l, a);
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, 4>, grid, block_ws, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, 4>, grid, block_ws, l, a);
     }
     if (a.qtok > 1)
         return paged ? launch_kernel(mfa_attn_split_kernel<false, true, true, false>, grid, block, l, a)

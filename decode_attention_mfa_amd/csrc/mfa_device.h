@@ -92,6 +92,7 @@ struct KvView {
     int32_t pt_stride;
     int32_t row_bytes;          // 256 * element size
     int32_t max_len;            // launch bound on sequence lengths
+    int32_t groups;             // K/V heads per token (1 for MFA; G for grouped-query caches)
 };
 
 // Length of sequence b as the kernels use it: seq_lens[b] clamped to
@@ -117,6 +118,19 @@ __device__ __forceinline__ int64_t kv_row(const KvView& kv, int b, int t) {
 template <bool PAGED>
 __device__ __forceinline__ int64_t kv_step_base(const KvView& kv, int b, int t0) {
     return kv_row<PAGED>(kv, b, t0);
+}
+
+// The same in K/V head g of a grouped cache: contiguous [B][G][kv_stride]
+// rows, pages [P][G][64] rows (G = kv.groups; g = 0 with G = 1 is
+// kv_step_base).
+template <bool PAGED>
+__device__ __forceinline__ int64_t kv_group_step_base(const KvView& kv, int b, int g, int t0) {
+    if constexpr (PAGED) {
+        const int32_t page = kv.page_table[(int64_t)b * kv.pt_stride + (t0 >> 6)];
+        return ((int64_t)page * kv.groups + g) * kPage;
+    } else {
+        return ((int64_t)b * kv.groups + g) * kv.kv_stride + t0;
+    }
 }
 
 }  // namespace mfa

@@ -32,7 +32,7 @@ struct AttnArgs {
     float* lse_out;         // [B][64] or nullptr
     float* part_o;          // workspace [B * n_chunk][64][256] fp32
     float* part_lse;        // workspace [B * n_chunk][64] fp32, base-2
-    int32_t* counters;      // workspace [B][nh] arrival counts, zero between calls
+    int32_t* counters;      // workspace [B][nh] arrival counts (nh <= 4), zero between calls
     int32_t chunk;          // tokens per split chunk, multiple of 64
     int32_t n_chunk;        // chunks per sequence slot in the launch = ceil(max_seq_len / chunk)
     int32_t fuse_max;       // sequences with 2..fuse_max chunks are merged in the attention kernel
@@ -43,7 +43,8 @@ struct AttnArgs {
     int32_t qtok;           // query tokens per sequence (1, or t for multi-token decode)
     int32_t fp8_mma;        // 1: FP8 MFMAs for S and P.V (quantised Q and P)
     int32_t part_stride;    // workspace partial slots per sequence (balanced mode)
-    int32_t nh;             // head groups per (query row set, chunk): 1, or 2 halves of 32 heads (FP8)
+    int32_t nh;             // workgroups per (query row set, chunk), each taking 64 / nh heads
+    int32_t kv_groups;      // K/V heads G of the cache (1: MFA); with G > 1, nh = G and workgroup i reads head i
 };
 
 // Balanced mode: each workgroup takes at least this many 64-token steps, so

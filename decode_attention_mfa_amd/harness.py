@@ -48,6 +48,7 @@ class DeviceCase:
     rms_eps: float = 1e-6
     split_tokens: int = 0
     min_len: int = 0             # lower bound of the lengths (as a scheduler knows it), 0 = unknown
+    kv_heads: int = 1            # K/V heads per token (grouped-query caches: 2 or 4)
 
     @property
     def paged(self) -> bool:
@@ -69,7 +70,8 @@ def to_device(case, device="cuda") -> DeviceCase:
         gamma=_dev(case.gamma, device), w_qb=_dev(case.w_qb, device),
         w_k=_dev(getattr(case, "w_k", None), device), w_v=_dev(getattr(case, "w_v", None), device),
         softmax_scale=case.softmax_scale, rms_eps=case.rms_eps, split_tokens=case.split_tokens,
-        min_len=max(0, int(case.seq_lens.min())) if case.batch else 0)
+        min_len=max(0, int(case.seq_lens.min())) if case.batch else 0,
+        kv_heads=getattr(case, "kv_heads", 1))
 
 
 def create_handle(dc: DeviceCase, *, max_batch: Optional[int] = None, max_context: Optional[int] = None,
@@ -79,7 +81,8 @@ def create_handle(dc: DeviceCase, *, max_batch: Optional[int] = None, max_contex
         page_size=64 if dc.paged else 0, max_batch=max_batch or dc.batch,
         max_context=max_context or dc.max_len,
         split_tokens=dc.split_tokens if split_tokens is None else split_tokens,
-        rms_eps=dc.rms_eps, softmax_scale=dc.softmax_scale, attn_math=attn_math))
+        rms_eps=dc.rms_eps, softmax_scale=dc.softmax_scale, attn_math=attn_math,
+        kv_heads=dc.kv_heads))
 
 
 def alloc_outputs(dc: DeviceCase):

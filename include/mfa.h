@@ -94,6 +94,15 @@ typedef struct {
     float rms_eps;         /* RMSNorm epsilon (1e-6), >= 0 */
     float softmax_scale;   /* score scale (1/16 = 1/sqrt(256)), finite and > 0 */
     int32_t attn_math;     /* enum mfa_attn_math; MFA_ATTN_FP8_MFMA needs an FP8 cache */
+    int32_t kv_heads;      /* K/V heads G: 0 or 1 = MFA's single shared K and V head; 2 or 4 =
+                              grouped-query attention ("GQA: Training Generalized Multi-Query
+                              Transformer Models from Multi-Head Checkpoints", named on the
+                              DeepSeek-V4 references), for comparing head-sharing schemes:
+                              query head h reads K/V head h / (64 / G), the cache holds G
+                              heads per token (layouts in mfa_kv). G > 1 needs an FP8 cache
+                              and MFA_ATTN_BF16_MFMA; mfa_decode only (not mfa_decode_mtp,
+                              mfa_kv_append or mfa_debug_gather_kv) and not
+                              MFA_SPLIT_BALANCED (else MFA_ERR_UNSUPPORTED) */
 } mfa_config;
 
 /* KV cache of one layer for one call (host struct describing device buffers).
@@ -102,6 +111,9 @@ typedef struct {
  *   paged (page_size 64): k, v are pools [num_pages][64][256] sharing page
  *     numbers; token t of sequence b is row t % 64 of page
  *     page_table[b * pt_stride + t / 64].
+ *   With G = kv_heads > 1: contiguous [batch][G][kv_stride][256] (head g of
+ *     token t at row (b * G + g) * kv_stride + t); paged pools
+ *     [num_pages][G][64][256] (row (page * G + g) * 64 + t % 64).
  * Element type: bf16 or E4M3 per the handle's kv_dtype. An FP8 element's
  * value is decode(code) * k_scale (keys) or * v_scale (values). Only rows
  * t < seq_lens[b] are read; mfa_kv_append writes row seq_lens[b]. */

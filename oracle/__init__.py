@@ -308,4 +308,5 @@ def case_attention(case, q: Optional[np.ndarray] = None, chunk: int = 0, nthread
     return attention(q, case.k, case.v, case.seq_lens,
                      kv_dtype=KV_FP8 if case.kv_dtype == "fp8" else KV_BF16,
                      k_scale=case.k_scale, v_scale=case.v_scale, page_table=case.page_table,
-                     softmax_scale=case.softmax_scale, chunk=chunk, nthreads=nthreads)
+                     softmax_scale=case.softmax_scale, chunk=chunk, nthreads=nthreads,
+                     kv_heads=getattr(case, "kv_heads", 1))

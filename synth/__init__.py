@@ -78,7 +78,9 @@ class Case:
 
     q      uint16 [B, H, D] bf16 bits (None when the case runs the Q projection)
     k, v   contiguous: [B, kv_stride, D]; paged: [num_pages, PAGE_SIZE, D];
-           uint16 (bf16 bits) or uint8 (E4M3FN codes)
+           uint16 (bf16 bits) or uint8 (E4M3FN codes). With kv_heads = G > 1
+           (grouped-query caches): [B, G, kv_stride, D] / [num_pages, G,
+           PAGE_SIZE, D]
     seq_lens int32 [B]; page_table int32 [B, pt_stride] or None
     k_scale, v_scale  float32 dequant scales (1.0 for bf16)
     x, w_qa, gamma, w_qb  bf16 bits for the Q projection, or None
@@ -104,6 +106,7 @@ class Case:
     rms_eps: float = 1e-6
     split_tokens: int = 0
     seed: int = 0
+    kv_heads: int = 1
 
     @property
     def paged(self) -> bool:
@@ -143,7 +146,8 @@ def _kv_tensor(g, shape, kv_dtype):
 def make_case(name: str, batch: int, seq_lens, kv_dtype: str = "bf16", *,
               seed: int = 0, paged: bool = False, with_qproj: bool = False,
               q_std: float = 1.0, split_tokens: int = 0, max_context: int = 0,
-              kv_slack: int = 0, append_room: int = 0, with_kv_proj: bool = False) -> Case:
+              kv_slack: int = 0, append_room: int = 0, with_kv_proj: bool = False,
+              kv_heads: int = 1) -> Case:
     """Build a case. ``seq_lens`` is an int or a sequence of B ints.
 
     Contiguous caches have ``kv_stride = max(L) + kv_slack`` token slots per
@@ -156,12 +160,15 @@ def make_case(name: str, batch: int, seq_lens, kv_dtype: str = "bf16", *,
     (contiguous: added to the slack; paged: pages cover L_b + append_room).
     ``with_kv_proj`` adds the hidden state x and the K and V projection
     weights, drawn like the Q projection's (std 1/sqrt(HIDDEN)).
+    ``kv_heads`` = G > 1 gives grouped-query caches with G K/V heads per token
+    (head axis after the sequence or page axis), drawn like the others.
     """
     st = _streams(seed)
     L = np.broadcast_to(np.asarray(seq_lens, dtype=np.int32), (batch,)).copy()
     maxL = int(L.max()) if batch else 0
     case = Case(name=name, batch=batch, kv_dtype=kv_dtype, seq_lens=L,
-                k=None, v=None, seed=seed, split_tokens=split_tokens)
+                k=None, v=None, seed=seed, split_tokens=split_tokens, kv_heads=kv_heads)
+    heads = (kv_heads,) if kv_heads > 1 else ()
     if paged:
         npg = (L.astype(np.int64) + append_room + PAGE_SIZE - 1) // PAGE_SIZE
         P = int(npg.sum())
@@ -174,9 +181,9 @@ def make_case(name: str, batch: int, seq_lens, kv_dtype: str = "bf16", *,
             pt[b, :n] = perm[off:off + n]
             off += n
         case.page_table = pt
-        shape = (max(P, 1), PAGE_SIZE, HEAD_DIM)
+        shape = (max(P, 1), *heads, PAGE_SIZE, HEAD_DIM)
     else:
-        shape = (batch, maxL + kv_slack + append_room, HEAD_DIM)
+        shape = (batch, *heads, maxL + kv_slack + append_room, HEAD_DIM)
     case.k, case.k_scale = _kv_tensor(st["k"], shape, kv_dtype)
     case.v, case.v_scale = _kv_tensor(st["v"], shape, kv_dtype)
     if with_qproj:
@@ -233,6 +240,18 @@ def config_case(i: int, *, batch: Optional[int] = None, scale_len: float = 1.0,
                      dtype=np.int32)
         return make_case("long_splitk", B, L, "bf16", seed=seed, q_std=q_std, split_tokens=512)
     raise ValueError(f"no workload {i}")
+
+
+def gqa_case(kv_heads: int, *, batch: Optional[int] = None, scale_len: float = 1.0,
+             paged: bool = False) -> Case:
+    """The FP8 workload's recipe (B = 128, L = 4096, N(0,1) Q and K/V, E4M3
+    codes with per-tensor amax scales) with ``kv_heads`` K/V heads per token,
+    for comparing head-sharing schemes at equal query shape. Seed 1003 for
+    one head (the FP8 workload itself), 1100 + G otherwise."""
+    B = batch or 128
+    seed = 1003 if kv_heads == 1 else 1100 + kv_heads
+    return make_case(f"fp8_gqa{kv_heads}", B, max(1, int(4096 * scale_len)), "fp8", seed=seed,
+                     paged=paged, kv_heads=kv_heads)
 
 
 def _with_append(base: Case) -> Case:

@@ -54,6 +54,11 @@ def _create(**kw):
     (dict(rms_eps=-1.0), -1, "rms_eps"),
     (dict(hidden=1000), -2, "hidden"),
     (dict(q_rank=100), -2, "q_rank"),
+    (dict(kv_heads=3, kv_dtype="fp8"), -1, "kv_heads"),
+    (dict(kv_heads=8, kv_dtype="fp8"), -1, "kv_heads"),
+    (dict(kv_heads=2, kv_dtype="bf16"), -2, "kv_heads > 1"),
+    (dict(kv_heads=2, kv_dtype="fp8", attn_math=1), -2, "kv_heads > 1"),
+    (dict(kv_heads=4, kv_dtype="fp8", split_tokens=-1), -2, "kv_heads > 1"),
 ])
 def test_create_rejects_bad_config(kw, status, needle):
     st, msg, h = _create(**kw)
