@@ -60,8 +60,7 @@ DESCRIPTION = {
 }
 # sources that decide the attention kernel's memory traffic (kernel, launch
 # shape, split and merge policy); the stored HBM counters hold for this hash
-ATTN_SOURCES = ("decode_attention_mfa_amd/csrc/mfa_attn.hip", "decode_attention_mfa_amd/csrc/mfa_attn_piece_setup.inc",
-                "decode_attention_mfa_amd/csrc/mfa_attn_piece_run.inc", "decode_attention_mfa_amd/csrc/mfa_attn_ws.inc",
+ATTN_SOURCES = ("decode_attention_mfa_amd/csrc/mfa_attn.hip", "decode_attention_mfa_amd/csrc/mfa_attn_ws.inc",
                 "decode_attention_mfa_amd/csrc/mfa_device.h",
                 "decode_attention_mfa_amd/csrc/mfa_internal.h", "decode_attention_mfa_amd/csrc/mfa_api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -69,11 +68,8 @@ WARMUP_SECONDS = 0.5
 
 
 def attn_kernel_name(split: int, fp8: bool) -> str:
-    """The attention kernel a launch runs: balanced split, or chunks (FP8
-    caches take the eight-wave kernel)."""
-    if split == 0:
-        return "mfa_attn_balanced_kernel"
-    return "mfa_attn_ws_split_kernel" if fp8 else "mfa_attn_split_kernel"
+    """The attention kernel a launch runs: balanced split, or chunks."""
+    return "mfa_attn_balanced_kernel" if split == 0 else "mfa_attn_ws_split_kernel"
 
 
 def log(*a):

@@ -5,28 +5,30 @@
 // log-sum-exp identity (Flash-Decoding, cited by title on the DeepSeek-V4
 // references).
 //
-// One workgroup (4 wave64s) owns a piece of one sequence: a chunk (chunked
-// kernel) or the part of its equal range of the batch's steps that falls in
-// that sequence (balanced kernel; see the notes before the two kernels). The
-// piece body (mfa_attn_piece_setup.inc, mfa_attn_piece_run.inc) walks the
-// piece in steps of 64 tokens (= one cache page):
-//   load  K and V rows of a step go from HBM straight into an LDS ring slot
-//         (global_load_lds_dwordx4, no registers); FP8 keeps 4 steps in
-//         flight, bf16 2. Wave w fetches rows 16w..16w+15 of both tensors.
-//   QK    wave w scores its 16 tokens against all 64 heads:
-//         S^T[16 tok x 64 heads] = K[16 x 256] . Q^T with bf16 MFMA 16x16x32,
-//         K rows from LDS as A operands (FP8 codes widened to bf16 in
-//         registers; every E4M3 value is exact in bf16), Q held in registers
-//         as B operands for the whole chunk. Each cached K byte feeds 64 heads.
-//   P     exp2 of the scaled scores against per-head reference maxima that
-//         stay fixed for a pass over the chunk (the exact maxima of its first
-//         step), rounded to bf16 into LDS. A score above its reference by more
-//         than kTau (base 2) makes the waves vote to redo the chunk with a
-//         higher reference, so the output is never rescaled inside the loop.
-//   PV    wave w owns output columns 64w..64w+63 of all 64 heads:
-//         O[64 x 64] += P[64 x 64 tok] . V[64 tok x 64], V read transposed
-//         from the shared tile with ds_read_b64_tr_b8 / _b16.
-// One workgroup barrier per step orders the ring, P and the vote.
+// One workgroup (eight wave64s, two per SIMD) owns a piece of one sequence:
+// a chunk (chunked kernel) or the part of its equal range of the batch's
+// steps that falls in that sequence (balanced kernel; see the notes before
+// the two kernels). The piece body (mfa_attn_ws.inc) walks the piece in
+// steps of 64 tokens (= one cache page), with the waves in two roles:
+//   score waves 0-3: wave w streams K rows 16w..16w+15 of each step from HBM
+//         into its own LDS region (global_load_lds_dwordx4, no registers) and
+//         scores them against all heads: S^T[16 tok x heads] = K . Q^T with
+//         bf16 MFMA 16x16x32, K rows from LDS as A operands (FP8 codes
+//         widened to bf16 in registers; every E4M3 value is exact in bf16), Q
+//         held in registers as B operands for the whole piece. Each cached K
+//         byte feeds 64 heads. Then P = exp2 of the scaled scores against
+//         per-head reference maxima that stay fixed for a pass over the piece
+//         (the exact maxima of its first step), rounded to bf16 into LDS. A
+//         score above its reference by more than kTau (base 2) makes the
+//         waves vote to redo the piece with a higher reference, so the output
+//         is never rescaled inside the loop.
+//   P.V waves 4-7: wave w streams V rows 16w..16w+15 into the shared V tile
+//         and owns output columns 64w..64w+63 of all heads:
+//         O[heads x 64] += P[heads x 64 tok] . V[64 tok x 64], V read
+//         transposed from the tile with ds_read_b64_tr_b8 / _b16.
+//   The roles run one step apart (scores of step s+1 beside the P.V of step
+//   s), so one wave's MFMAs overlap the other's VALU work; one workgroup
+//   barrier per step orders the ring, P and the vote.
 //
 // Scores are kept in the base-2 domain: s2 = s * log2(e), exp -> exp2.
 // Output of a piece: for a one-piece sequence the final bf16 output and lse;
@@ -176,64 +178,13 @@ __device__ __forceinline__ void wait_vmem() {
 // them on one XCD at about the same time: the KV bytes come from HBM once and
 // from that XCD's L2 for the other tokens.
 
-template <bool FP8, bool PAGED, bool MTP, bool F8MMA>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void mfa_attn_split_kernel(const AttnArgs p) {
-#define MFA_PIECE_TID threadIdx.x
-#include "mfa_attn_piece_setup.inc"
-#undef MFA_PIECE_TID
-
-    int b, c, kvb, L;
-    if constexpr (!MTP) {
-        b = blockIdx.x / p.n_chunk;
-        c = blockIdx.x - b * p.n_chunk;
-        kvb = b;
-        L = seq_len(p.kv, b);
-    } else {
-        const int t = p.qtok;
-        const int grp = blockIdx.x / (8 * t);
-        const int r = blockIdx.x - grp * 8 * t;
-        const int wi = grp * 8 + (r & 7);   // (sequence, chunk) work item
-        if (wi >= p.batch * p.n_chunk) return;
-        kvb = wi / p.n_chunk;
-        c = wi - kvb * p.n_chunk;
-        const int j = r >> 3;
-        b = kvb * t + j;
-        L = max(0, seq_len(p.kv, kvb) - (t - 1 - j));
-    }
-    const int t_begin = c * p.chunk;
-
-    if (t_begin >= L) {
-        if (c == 0) {  // empty sequence: out = 0, lse = -inf
-            uint16_t* ob = p.out + (int64_t)b * kHeads * kHeadDim;
-            for (int i = tid; i < kHeads * kHeadDim / 8; i += 256)
-                reinterpret_cast<u32x4*>(ob)[i] = u32x4{0, 0, 0, 0};
-            if (p.lse_out && tid < kHeads)
-                p.lse_out[b * kHeads + tid] = -__builtin_inff();
-        }
-        return;
-    }
-    const int t_end = min(L, t_begin + p.chunk);
-    const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
-    const int last_s = nsteps - 1;
-    const bool single = (L + p.chunk - 1) / p.chunk == 1;
-
-#define MFA_PIECE_K c
-#define MFA_PIECE_NPARTS ((L + p.chunk - 1) / p.chunk)
-#define MFA_PIECE_BASE ((int64_t)b * p.n_chunk)
-#include "mfa_attn_piece_run.inc"
-#undef MFA_PIECE_K
-#undef MFA_PIECE_NPARTS
-#undef MFA_PIECE_BASE
-}
-
-// FP8 caches: the same work split, eight waves in two roles (the body in
+// The chunked kernel: eight waves in two roles (the body in
 // mfa_attn_ws.inc). With several workgroups per (sequence, chunk) -- the t
 // query tokens of multi-token decode, or p.nh groups of 16 * NHT heads --
 // those workgroups get block indices 8 apart inside a group of 8 times their
 // number, so that the round-robin dispatch puts them on one XCD at about the
 // same time (their shared K/V rows then come from HBM once).
-template <bool PAGED, bool MTP, bool F8MMA, int NHT>
+template <bool FP8, bool PAGED, bool MTP, bool F8MMA, int NHT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void mfa_attn_ws_split_kernel(const AttnArgs p) {
     int b, c, kvb, L, part = 0;
@@ -302,12 +253,6 @@ __device__ __forceinline__ int opaque_thread_index() {
 // whose partials sit at workspace slots part_base + 0 .. nparts-1.
 template <bool FP8, bool PAGED, bool F8MMA>
 __device__ __forceinline__ void attend_piece(const AttnArgs& p, const int b, const int L, const int t_begin,
-                                             const int t_end, const int piece_k, const int nparts,
-                                             const int64_t part_base);
-
-// FP8 caches: the wave-specialized body (512 threads).
-template <bool PAGED, bool F8MMA>
-__device__ __forceinline__ void attend_piece_ws(const AttnArgs& p, const int b, const int L, const int t_begin,
                                                 const int t_end, const int piece_k, const int nparts,
                                                 const int64_t part_base) {
     constexpr int NHT = 4;
@@ -327,28 +272,6 @@ __device__ __forceinline__ void attend_piece_ws(const AttnArgs& p, const int b, 
 #undef MFA_PIECE_BASE
 }
 
-template <bool FP8, bool PAGED, bool F8MMA>
-__device__ __forceinline__ void attend_piece(const AttnArgs& p, const int b, const int L, const int t_begin,
-                                             const int t_end, const int piece_k, const int nparts,
-                                             const int64_t part_base) {
-#define MFA_PIECE_TID opaque_thread_index()
-#include "mfa_attn_piece_setup.inc"
-#undef MFA_PIECE_TID
-
-    const int kvb = b;
-    const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
-    const int last_s = nsteps - 1;
-    const bool single = nparts == 1;
-
-#define MFA_PIECE_K piece_k
-#define MFA_PIECE_NPARTS nparts
-#define MFA_PIECE_BASE part_base
-#include "mfa_attn_piece_run.inc"
-#undef MFA_PIECE_K
-#undef MFA_PIECE_NPARTS
-#undef MFA_PIECE_BASE
-}
-
 // out = 0, lse = -inf for an empty sequence.
 __device__ __forceinline__ void write_empty(const AttnArgs& p, int b) {
     uint16_t* ob = p.out + (int64_t)b * kHeads * kHeadDim;
@@ -358,10 +281,9 @@ __device__ __forceinline__ void write_empty(const AttnArgs& p, int b) {
 }
 
 template <bool FP8, bool PAGED, bool F8MMA>
-__global__ __attribute__((amdgpu_flat_work_group_size(FP8 ? 512 : 256, FP8 ? 512 : 256),
-                          amdgpu_waves_per_eu(FP8 ? 2 : 1, FP8 ? 2 : 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void mfa_attn_balanced_kernel(const AttnArgs p) {
-    constexpr int NT = FP8 ? 512 : 256;   // threads
+    constexpr int NT = 512;               // threads
     constexpr int NW = NT / 64;           // waves
     __shared__ int wave_total[NW];
     __shared__ int first_seq[3];
@@ -446,14 +368,9 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
             if (n > 0) {
                 const int seg_end = min(s_hi, Pq + n);
                 const int first = Pq / per, last = (Pq + n - 1) / per;
-                if constexpr (FP8)
-                    attend_piece_ws<PAGED, F8MMA>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
-                                                  (int)blockIdx.x - first, last - first + 1,
-                                                  (int64_t)bq * p.part_stride);
-                else
-                    attend_piece<FP8, PAGED, F8MMA>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
-                                                    (int)blockIdx.x - first, last - first + 1,
-                                                    (int64_t)bq * p.part_stride);
+                attend_piece<FP8, PAGED, F8MMA>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
+                                                (int)blockIdx.x - first, last - first + 1,
+                                                (int64_t)bq * p.part_stride);
                 s = seg_end;
                 if (s >= s_hi) break;
                 __syncthreads();   // the piece is done with the LDS
@@ -553,42 +470,42 @@ __global__ __launch_bounds__(256) void mfa_gather_kernel(const KvView kv, int b,
 }
 
 hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l) {
-    const dim3 grid(workgroups), block(256), block_ws(512);
+    const dim3 grid(workgroups), block(512);
     if (a.fp8_mma) {   // FP8 cache only (checked by the caller)
         if (a.balanced)
-            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, true>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_balanced_kernel<true, false, true>, grid, block_ws, l, a);
+            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, true>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_balanced_kernel<true, false, true>, grid, block, l, a);
         if (a.nh == 2)
-            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true, 2>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, 2>, grid, block_ws, l, a);
-        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, true, 4>, grid, block_ws, l, a)
-                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, 4>, grid, block_ws, l, a);
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, true, 2>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<true, false, false, true, 2>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, true, 4>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<true, false, false, true, 4>, grid, block, l, a);
     }
     if (a.balanced) {
         if (fp8)
-            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, false>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_balanced_kernel<true, false, false>, grid, block_ws, l, a);
+            return paged ? launch_kernel(mfa_attn_balanced_kernel<true, true, false>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_balanced_kernel<true, false, false>, grid, block, l, a);
         return paged ? launch_kernel(mfa_attn_balanced_kernel<false, true, false>, grid, block, l, a)
                      : launch_kernel(mfa_attn_balanced_kernel<false, false, false>, grid, block, l, a);
     }
-    if (fp8) {
-        if (a.qtok > 1)   // bf16 MFMAs, all 64 heads per workgroup (checked by the caller)
-            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, 4>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_ws_split_kernel<false, true, false, 4>, grid, block_ws, l, a);
-        if (a.nh == 4)    // grouped-query caches with four K/V heads
-            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, 1>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, 1>, grid, block_ws, l, a);
-        if (a.nh == 2)
-            return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, 2>, grid, block_ws, l, a)
-                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, 2>, grid, block_ws, l, a);
-        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, false, false, 4>, grid, block_ws, l, a)
-                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, 4>, grid, block_ws, l, a);
+    if (!fp8) {
+        if (a.qtok > 1)
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<false, true, true, false, 4>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, false, 4>, grid, block, l, a);
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<false, true, false, false, 4>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, false, 4>, grid, block, l, a);
     }
-    if (a.qtok > 1)
-        return paged ? launch_kernel(mfa_attn_split_kernel<false, true, true, false>, grid, block, l, a)
-                     : launch_kernel(mfa_attn_split_kernel<false, false, true, false>, grid, block, l, a);
-    return paged ? launch_kernel(mfa_attn_split_kernel<false, true, false, false>, grid, block, l, a)
-                 : launch_kernel(mfa_attn_split_kernel<false, false, false, false>, grid, block, l, a);
+    if (a.qtok > 1)   // bf16 MFMAs, all 64 heads per workgroup (checked by the caller)
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, true, false, 4>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<true, false, true, false, 4>, grid, block, l, a);
+    if (a.nh == 4)    // grouped-query caches with four K/V heads
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, false, 1>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<true, false, false, false, 1>, grid, block, l, a);
+    if (a.nh == 2)
+        return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, false, 2>, grid, block, l, a)
+                     : launch_kernel(mfa_attn_ws_split_kernel<true, false, false, false, 2>, grid, block, l, a);
+    return paged ? launch_kernel(mfa_attn_ws_split_kernel<true, true, false, false, 4>, grid, block, l, a)
+                 : launch_kernel(mfa_attn_ws_split_kernel<true, false, false, false, 4>, grid, block, l, a);
 }
 
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l) {
