@@ -310,3 +310,22 @@ def test_graph_replay_matches_eager(split):
         assert row_err(hz.bf16_to_f64(out), o_ref) <= TOL
     finally:
         m.mfa_destroy(h)
+
+
+@pytest.mark.parametrize("trial", range(8))
+def test_seeded_random_configurations(trial):
+    """Seeded random mixes of batch size, lengths (empty, one token, page
+    boundaries, long), cache type and layout, and split (chunks of any page
+    multiple, automatic, balanced) against the oracle, so that combinations
+    no hand-written case covers still get checked."""
+    rng = np.random.default_rng(900 + trial)
+    B = int(rng.integers(1, 9))
+    pool = [0, 1, 2, 63, 64, 65, 127, 128, 129, 500, 1024, 1500, 2048, 2100, 3000]
+    L = [int(rng.choice(pool)) if rng.random() < 0.6 else int(rng.integers(1, 3200)) for _ in range(B)]
+    if max(L) == 0:
+        L[0] = 1
+    kv = "fp8" if rng.random() < 0.6 else "bf16"
+    paged = bool(rng.random() < 0.5)
+    split = int(rng.choice([0, 64, 128, 320, 1024, -1]))
+    case = synth.make_case("random", B, L, kv, seed=910 + trial, paged=paged, kv_slack=int(rng.integers(0, 9)))
+    check_parity(case, split_tokens=split, label=f"random trial {trial}: L={L} {kv} paged={paged}")
