@@ -227,11 +227,11 @@ int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v,
 int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len);
 
 /* The number of workgroups that share the 64 query heads of one (sequence,
- * chunk) in that split: 1, or 2 (heads 0-31 and 32-63, which then read the
- * same K/V rows, the second read from L2). Two only with attn_math
- * MFA_ATTN_FP8_MFMA and a chunked split whose doubled grid fits on the
- * compute units at once; the result of mfa_decode does not depend on it.
- * Negative status on error. */
+ * chunk) in that split: 1; 2 (heads 0-31 and 32-63, which then read the same
+ * K/V rows, the second read from L2) with attn_math MFA_ATTN_FP8_MFMA and a
+ * chunked split whose doubled grid fits on the compute units at once; or
+ * kv_heads for a grouped-query cache (one workgroup per K/V head). The
+ * result of mfa_decode does not depend on it. Negative status on error. */
 int32_t mfa_head_groups(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len);
 
 /* Test support: copy the logical K and V rows t < L_b of sequence b into
