@@ -112,7 +112,7 @@ __device__ __forceinline__ const uint8_t* wave_uniform(const uint8_t* ptr) {
 // per-XCD L2, so a workgroup on another XCD sees the data once the store is
 // acknowledged. The loads are issued as one asm block that also waits for
 // them, so no output register is left pending when the block ends.
-__device__ __forceinline__ void coherent_store_b128(f32x4* ptr, f32x4 v) {
+__device__ __forceinline__ void coherent_store_b128(u32x4* ptr, u32x4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(ptr), "v"(v) : "memory");
 }
 __device__ __forceinline__ void coherent_load_b128x8(f32x4* v, const f32x4* src, int stride) {
@@ -132,6 +132,16 @@ __device__ __forceinline__ void coherent_load_b128x8(f32x4* v, const f32x4* src,
         : "memory");
 }
 
+__device__ __forceinline__ void coherent_load_b128x2(f32x4* v, const f32x4* src, int stride) {
+    asm volatile(
+        "global_load_dwordx4 %0, %2, off sc1\n\t"
+        "global_load_dwordx4 %1, %3, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1])
+        : "v"(src), "v"(src + stride)
+        : "memory");
+}
+
 __device__ __forceinline__ void coherent_load_b128x4(f32x4* v, const f32x4* src, int stride) {
     asm volatile(
         "global_load_dwordx4 %0, %4, off sc1\n\t"
@@ -142,6 +152,15 @@ __device__ __forceinline__ void coherent_load_b128x4(f32x4* v, const f32x4* src,
         : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
         : "v"(src), "v"(src + stride), "v"(src + 2 * stride), "v"(src + 3 * stride)
         : "memory");
+}
+
+// Rows 2j and 2j + 1 (four columns each) of a bf16 dump group: the low half
+// of each word is the first of its two values.
+__device__ __forceinline__ void unpack_bf16_rows(u32x4 d, f32x4& r0, f32x4& r1) {
+    r0 = f32x4{__builtin_bit_cast(float, d.x << 16), __builtin_bit_cast(float, d.x & 0xffff0000u),
+               __builtin_bit_cast(float, d.y << 16), __builtin_bit_cast(float, d.y & 0xffff0000u)};
+    r1 = f32x4{__builtin_bit_cast(float, d.z << 16), __builtin_bit_cast(float, d.z & 0xffff0000u),
+               __builtin_bit_cast(float, d.w << 16), __builtin_bit_cast(float, d.w & 0xffff0000u)};
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
