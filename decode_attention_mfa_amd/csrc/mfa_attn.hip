@@ -413,9 +413,9 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
 //   M = max_c lse2_c, W_c = 2^(lse2_c - M), out = sum_c W_c o_c / sum_c W_c,
 //   lse = (M + log2 sum_c W_c) * ln 2.
 // One wave per (sequence, head); lane t owns columns 4t..4t+3. The chunk
-// weights go through LDS; the partial rows (1 KB per chunk, contiguous) are
-// read kCombineUnroll at a time so that many loads are in flight. Chunks are
-// accumulated in index order.
+// weights go through LDS; the partial rows (bf16, 512 bytes per chunk,
+// contiguous) are read kCombineUnroll at a time so that many loads are in
+// flight. Chunks are accumulated in index order.
 constexpr int kCombineUnroll = 16;
 constexpr int kCombineBlock = 1024;   // chunk weights staged per round
 __global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
@@ -429,8 +429,12 @@ __global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
     if (nc <= p.fuse_max) return;   // merged by the attention kernel itself
     const int64_t base = (int64_t)b * p.n_chunk;
     const float* lse = p.part_lse + base * kHeads + h;   // chunk c at lse[c * kHeads]
-    constexpr int64_t kRow = kHeads * kHeadDim / 4;      // f32x4 per chunk partial
-    const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + (base * kHeads + h) * (kHeadDim / 4) + t;
+    constexpr int64_t kRow = kHeads * kHeadDim / 4;      // 8-byte groups per chunk partial
+    const u32x2* po = reinterpret_cast<const u32x2*>(p.part_o) + (base * kHeads + h) * (kHeadDim / 4) + t;
+    auto row = [](u32x2 d) {
+        return f32x4{__builtin_bit_cast(float, d.x << 16), __builtin_bit_cast(float, d.x & 0xffff0000u),
+                     __builtin_bit_cast(float, d.y << 16), __builtin_bit_cast(float, d.y & 0xffff0000u)};
+    };
 
     float M = -__builtin_inff();
     for (int c = t; c < nc; c += 64) M = fmaxf(M, lse[(int64_t)c * kHeads]);
@@ -449,13 +453,13 @@ __global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
         __syncthreads();
         int i = 0;
         for (; i + kCombineUnroll <= n; i += kCombineUnroll) {
-            f32x4 v[kCombineUnroll];
+            u32x2 v[kCombineUnroll];
 #pragma unroll
             for (int j = 0; j < kCombineUnroll; j++) v[j] = po[(int64_t)(c0 + i + j) * kRow];
 #pragma unroll
-            for (int j = 0; j < kCombineUnroll; j++) acc += wts[i + j] * v[j];
+            for (int j = 0; j < kCombineUnroll; j++) acc += wts[i + j] * row(v[j]);
         }
-        for (; i < n; i++) acc += wts[i] * po[(int64_t)(c0 + i) * kRow];
+        for (; i < n; i++) acc += wts[i] * row(po[(int64_t)(c0 + i) * kRow]);
         __syncthreads();
     }
     float wsum = wpart;
