@@ -53,7 +53,7 @@ struct mfa_ctx {
     int device;
     int num_cu;
     int max_chunks;        // per sequence, at the smallest chunk this handle may use
-    float* part_o;         // [max_batch * max_chunks][64][256]
+    float* part_o;         // [max_batch * max_chunks][64][256] bf16
     float* part_lse;       // [max_batch * max_chunks][64]
     int32_t* counters;     // [max_batch][2], zero between calls
     float* c_part;         // [hidden / kQprojRowsPerSplit][max_batch][q_rank]
@@ -219,7 +219,7 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     // one more slot per sequence than chunks: a balanced split may cut a
     // sequence into ceil(steps / 4) + 1 pieces
     const int64_t nparts = (int64_t)c.max_batch * (max_chunks + 1);
-    const int64_t bytes_o = nparts * mfa::kHeads * mfa::kHeadDim * 4;
+    const int64_t bytes_o = nparts * mfa::kHeads * mfa::kHeadDim * 2;   // bf16 partials
     const int64_t bytes_lse = nparts * mfa::kHeads * 4;
     const int64_t bytes_c = (int64_t)(c.hidden / mfa::kQprojRowsPerSplit) * c.max_batch * c.q_rank * 4;
     const int64_t bytes_chat = (int64_t)c.max_batch * c.q_rank * 2;

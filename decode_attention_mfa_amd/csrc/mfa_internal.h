@@ -30,7 +30,7 @@ struct AttnArgs {
     KvView kv;
     uint16_t* out;          // [B][64][256] bf16
     float* lse_out;         // [B][64] or nullptr
-    float* part_o;          // workspace: B * n_chunk slots of 64 KB; bf16 [64][256] partial rows (mfa_combine_kernel) or bf16 dumps of in-kernel merges
+    float* part_o;          // workspace: B * n_chunk slots of 32 KB; bf16 [64][256] partial rows (mfa_combine_kernel) or bf16 dumps of in-kernel merges
     float* part_lse;        // workspace [B * n_chunk][64] fp32, base-2
     int32_t* counters;      // workspace [B][nh] arrival counts (nh <= 4), zero between calls
     int32_t chunk;          // tokens per split chunk, multiple of 64

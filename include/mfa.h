@@ -137,10 +137,12 @@ typedef struct {
 
 /* Create a handle for one layer shape. Validates `cfg` (host pointer) and
  * allocates the split-K workspace on the current device:
- *   max_batch * (ceil(max_context / C) + 1) * 64 * (256 + 1) * 4 bytes of
- *   chunk partials, C = split_tokens when positive, else 256 (the smallest
- *   piece a per-call choice or a balanced split makes), max_batch 4-byte arrival counters (zeroed here, left
- *   at zero by every call), Q-projection scratch of
+ *   max_batch * (ceil(max_context / C) + 1) * 64 * (256 * 2 + 4) bytes of
+ *   chunk partials (bf16 rows and fp32 log-sum-exps), C = split_tokens when
+ *   positive, else 256 (the smallest piece a per-call choice or a balanced
+ *   split makes), 4 * max_batch 4-byte arrival counters (one per query row
+ *   and head group; zeroed here, left at zero by every call), Q-projection
+ *   scratch of
  *   max_batch * q_rank * (4 * hidden / 512 + 2) + (q_rank / 64) * (max_batch
  *   + ceil(max_batch / 32)) * 4 bytes (its arrival counters zeroed here and
  *   left at zero), and K/V-projection partials of
