@@ -32,10 +32,11 @@
 //
 // Scores are kept in the base-2 domain: s2 = s * log2(e), exp -> exp2.
 // Output of a piece: for a one-piece sequence the final bf16 output and lse;
-// otherwise the piece-normalised output (fp32) and its base-2 lse, merged by
-// the log-sum-exp identity either here, by the last of the sequence's pieces
-// to finish (balanced launches, and chunked launches where no sequence has
-// more than two chunks), or by mfa_combine_kernel afterwards.
+// otherwise the piece-normalised output (rounded to bf16) and its base-2 lse
+// (fp32), merged in fp32 by the log-sum-exp identity either here, by the last
+// of the sequence's pieces to finish (balanced launches, and chunked launches
+// where no sequence has more than two chunks), or by mfa_combine_kernel
+// afterwards.
 #include <type_traits>
 
 #include "mfa_device.h"

@@ -99,9 +99,9 @@ struct GemmEpi {
     int32_t rank;
 };
 
-// The down-projection splits K into blocks of this many rows (one
-// workgroup each, fp32 partials summed by the RMSNorm kernel); hidden must be
-// a multiple of it.
+// The down-projection splits K into blocks of this many rows or twice as many
+// (one workgroup each per column block; fp32 partials, summed by the last
+// workgroup of the column block to finish); hidden must be a multiple of it.
 constexpr int kQprojRowsPerSplit = 512;
 
 struct KvAppendArgs {

@@ -175,9 +175,10 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
  * (or a per-call choice when split_tokens is 0), or by a balanced split
  * (MFA_SPLIT_BALANCED, and the per-call choice for batches of at least half
  * the CU count whose length bounds do not show equal step counts) into the
- * pieces that equal ranges of steps over the whole batch give; partials go to
- * the handle's workspace and are merged by the log-sum-exp identity, in
- * chunk order: inside the attention kernel by the last chunk to finish when
+ * pieces that equal ranges of steps over the whole batch give; partials
+ * (normalised, rounded to bf16, with fp32 log-sum-exps) go to the handle's
+ * workspace and are merged in fp32 by the log-sum-exp identity, in chunk
+ * order: inside the attention kernel by the last chunk to finish when
  * no sequence of the call has more than two chunks or the split is balanced,
  * else by a second kernel on the same stream. The result depends only on the
  * logical K/V values, the lengths and the chunking, not on the cache layout:
