@@ -430,7 +430,8 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
         a.fuse_max = 1 << 30;   // the last piece of a sequence always merges
         a.nh = 1;
         a.kv_groups = 1;
-        const int64_t bound = (int64_t)batch * ((max_len + mfa::kStep - 1) / mfa::kStep);
+        // units the ranges deal out (steps plus the per-sequence piece cost)
+        const int64_t bound = (int64_t)batch * ((max_len + mfa::kStep - 1) / mfa::kStep + mfa::kBalancedPieceCost);
         int64_t g = h->num_cu;
         if (bound > g * mfa::kMaxPagedChunkSteps) g = round_up((bound + mfa::kMaxPagedChunkSteps - 1) / mfa::kMaxPagedChunkSteps, h->num_cu);
         workgroups = (int)g;

@@ -314,8 +314,14 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
     const int B = p.batch;
     const int G = gridDim.x;
     auto steps_of_len = [](int len) { return (len + kStep - 1) / kStep; };
+    // a sequence's share of the ranges: its steps plus kBalancedPieceCost
+    // units for the fixed work of its piece (none when it is empty)
+    auto units_of_len = [&](int len) {
+        const int n = steps_of_len(len);
+        return n > 0 ? n + kBalancedPieceCost : 0;
+    };
 
-    // prefix of the step counts over sequences: thread t sums sequences
+    // prefix of the unit counts over sequences: thread t sums sequences
     // [t*per_t, (t+1)*per_t) (up to four lengths kept in registers, so
     // the lengths are read once), then a scan across the workgroup
     constexpr int kRegLens = 4;
@@ -335,7 +341,7 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
 #pragma unroll
         for (int i = 0; i < kRegLens; i++) {
             lens[i] = b0 + i < b1 ? seq_len(p.kv, b0 + i) : 0;
-            cnt += steps_of_len(lens[i]);
+            cnt += units_of_len(lens[i]);
         }
 #pragma unroll
         for (int i = 0; i < kRegLens; i++)
@@ -343,7 +349,7 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
     } else {
         for (int bb = b0; bb < b1; bb++) {
             const int len = seq_len(p.kv, bb);
-            cnt += steps_of_len(len);
+            cnt += units_of_len(len);
             note_empty(bb, len);
         }
     }
@@ -364,12 +370,12 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
     const int s_lo = blockIdx.x * per;
     const int s_hi = min(total, s_lo + per);
     if (s_lo < total) {
-        // the sequence holding step s_lo, its first step and its length
+        // the sequence holding unit s_lo, its first unit and its length
         if (excl <= s_lo && s_lo < excl + cnt) {
             int P = excl;
             for (int bb = b0; bb < b1; bb++) {
                 const int len = per_t <= kRegLens ? lens[min(bb - b0, kRegLens - 1)] : seq_len(p.kv, bb);
-                const int n = steps_of_len(len);
+                const int n = units_of_len(len);
                 if (s_lo < P + n) {
                     first_seq[0] = bb;
                     first_seq[1] = P;
@@ -383,19 +389,23 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
         int bq = __builtin_amdgcn_readfirstlane(first_seq[0]);
         int Pq = __builtin_amdgcn_readfirstlane(first_seq[1]);
         int L = __builtin_amdgcn_readfirstlane(first_seq[2]);
-        for (int s = s_lo;;) {
+        // sequence bq takes units [Pq, Pq + units): the piece cost first,
+        // then its steps from unit r0 = Pq + kBalancedPieceCost on
+        for (;;) {
             const int n = steps_of_len(L);
             if (n > 0) {
-                const int seg_end = min(s_hi, Pq + n);
-                const int first = Pq / per, last = (Pq + n - 1) / per;
-                attend_piece<FP8, PAGED, F8MMA>(p, bq, L, (s - Pq) * kStep, min(L, (seg_end - Pq) * kStep),
-                                                (int)blockIdx.x - first, last - first + 1,
-                                                (int64_t)bq * p.part_stride);
-                s = seg_end;
-                if (s >= s_hi) break;
-                __syncthreads();   // the piece is done with the LDS
+                const int r0 = Pq + kBalancedPieceCost;
+                const int lo = max(s_lo, r0), hi = min(s_hi, r0 + n);
+                if (hi > lo) {
+                    const int first = r0 / per, last = (r0 + n - 1) / per;
+                    attend_piece<FP8, PAGED, F8MMA>(p, bq, L, (lo - r0) * kStep, min(L, (hi - r0) * kStep),
+                                                    (int)blockIdx.x - first, last - first + 1,
+                                                    (int64_t)bq * p.part_stride);
+                }
+                if (r0 + n >= s_hi) break;
+                if (hi > lo) __syncthreads();   // the piece is done with the LDS
             }
-            Pq += n;
+            Pq += units_of_len(L);
             bq++;
             L = seq_len(p.kv, bq);
         }

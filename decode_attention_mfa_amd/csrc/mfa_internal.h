@@ -52,6 +52,12 @@ struct AttnArgs {
 // workspace holds ceil(max_context / 256) + 1 partial slots per sequence).
 constexpr int kMinBalancedSteps = 4;
 
+// Balanced mode: the ranges deal out units, a sequence's steps plus this many
+// for the fixed work of its piece (the Q fetch, the ring's first loads, the
+// first step's maxima, the epilogue), so that a range holding the starts of
+// several short sequences gets fewer steps.
+constexpr int kBalancedPieceCost = 3;
+
 // Multi-token decode: at most this many query tokens per sequence.
 constexpr int kMaxQueryTokens = 16;
 
