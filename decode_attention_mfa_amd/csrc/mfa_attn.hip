@@ -447,34 +447,6 @@ __global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
                      __builtin_bit_cast(float, d.y << 16), __builtin_bit_cast(float, d.y & 0xffff0000u)};
     };
 
-    uint16_t* orow = p.out + ((int64_t)b * kHeads + h) * kHeadDim + 4 * t;
-    if (nc <= kCombineUnroll) {
-        // few chunks: every partial row (index clamped to the last chunk) and
-        // lane c's lse in flight at once, one memory round trip; chunk c's
-        // weight comes from lane c. Same arithmetic, in the same order, as
-        // the general path below.
-        u32x2 v[kCombineUnroll];
-#pragma unroll
-        for (int j = 0; j < kCombineUnroll; j++) v[j] = po[(int64_t)min(j, nc - 1) * kRow];
-        const float lv = t < nc ? lse[(int64_t)t * kHeads] : -__builtin_inff();
-        float M = lv;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-        const float wv = t < nc ? __builtin_amdgcn_exp2f(lv - M) : 0.f;
-        float wsum = wv;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kCombineUnroll; j++)
-            if (j < nc) acc += __shfl(wv, j) * row(v[j]);
-        const float inv = 1.f / wsum;
-        *reinterpret_cast<u32x2*>(orow) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
-                                               pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-        if (p.lse_out && t == 0) p.lse_out[b * kHeads + h] = (M + __builtin_amdgcn_logf(wsum)) * kLn2;
-        return;
-    }
-
     float M = -__builtin_inff();
     for (int c = t; c < nc; c += 64) M = fmaxf(M, lse[(int64_t)c * kHeads]);
 #pragma unroll
@@ -505,6 +477,7 @@ __global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
     const float inv = 1.f / wsum;
+    uint16_t* orow = p.out + ((int64_t)b * kHeads + h) * kHeadDim + 4 * t;
     *reinterpret_cast<u32x2*>(orow) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
                                            pack_bf16x2(acc[2] * inv, acc[3] * inv)};
     if (p.lse_out && t == 0) p.lse_out[b * kHeads + h] = (M + __builtin_amdgcn_logf(wsum)) * kLn2;
