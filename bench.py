@@ -207,8 +207,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the MFA decode path has no multi-GPU mode here)", file=sys.stderr)
+        print(f"bench.py: the MFA decode path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(there is no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
