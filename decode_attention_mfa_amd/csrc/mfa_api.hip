@@ -421,8 +421,8 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
     a.fp8_mma = h->cfg.attn_math == MFA_ATTN_FP8_MFMA ? 1 : 0;
     int workgroups;
     if (qtok == 1 && use_balanced(h, batch, max_len, kv->min_seq_len)) {
-        // equal ranges of at least 4 and at most 128 steps: one workgroup per
-        // CU, or more when the batch's steps could exceed 128 per workgroup
+        // equal ranges of at least 4 and at most 128 units: one workgroup per
+        // CU, or more when the batch's units could exceed 128 per workgroup
         a.balanced = 1;
         a.chunk = 0;
         a.n_chunk = 0;

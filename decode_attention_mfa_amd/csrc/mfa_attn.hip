@@ -176,15 +176,16 @@ __device__ __forceinline__ void wait_vmem() {
 
 // ------------------------------------------------------------ the two kernels
 // Two ways to cut the work into workgroups:
-//   chunks   (mfa_attn_split_kernel): workgroup (b, c) takes tokens
+//   chunks   (mfa_attn_ws_split_kernel): workgroup (b, c) takes tokens
 //            [c*chunk, (c+1)*chunk) of sequence b; workgroups past L_b exit.
-//   balanced (mfa_attn_balanced_kernel): the 64-token steps of all sequences,
-//            in sequence order, are dealt out in equal ranges of `per` steps
-//            (per = ceil(total / workgroups), at least kMinBalancedSteps, at
-//            most kMaxPagedChunkSteps), so every workgroup streams the same
-//            number of bytes whatever the lengths (the work-centric
-//            decomposition of Stream-K, cited by title on the DeepSeek-V4
-//            references, applied to KV steps). A range may hold the end of one
+//   balanced (mfa_attn_balanced_kernel): all sequences, in sequence order,
+//            laid end to end as units (a sequence's 64-token steps plus
+//            kBalancedPieceCost for its piece's fixed work), are dealt out
+//            in equal ranges of `per` units (per = ceil(total / workgroups),
+//            at least kMinBalancedSteps, at most kMaxPagedChunkSteps), so
+//            every workgroup does about the same work whatever the lengths
+//            (the work-centric decomposition of Stream-K, cited by title on
+//            the DeepSeek-V4 references, applied to KV steps). A range may hold the end of one
 //            sequence and the start of others; each piece is a call of
 //            attend_piece, and the last of a sequence's pieces to finish
 //            merges them.

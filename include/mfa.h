@@ -70,10 +70,11 @@ enum mfa_attn_math {
 
 typedef struct mfa_ctx* mfa_handle;
 
-/* mfa_config.split_tokens value: cut the work of each call into equal ranges
- * of 64-token steps, one range per workgroup, over all sequences in order
- * (the work-centric decomposition of Stream-K, cited by title on the
- * DeepSeek-V4 references), whatever the lengths. A sequence cut into several
+/* mfa_config.split_tokens value: cut the work of each call into equal ranges,
+ * one per workgroup, over all sequences in order (the work-centric
+ * decomposition of Stream-K, cited by title on the DeepSeek-V4 references),
+ * whatever the lengths. A sequence counts its 64-token steps plus a fixed
+ * cost of 8 for its piece's set-up and epilogue. A sequence cut into several
  * pieces is merged by the last piece to finish, in piece order. */
 #define MFA_SPLIT_BALANCED (-1)
 
@@ -175,7 +176,7 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
  * (or a per-call choice when split_tokens is 0), or by a balanced split
  * (MFA_SPLIT_BALANCED, and the per-call choice for batches of at least half
  * the CU count whose length bounds do not show equal step counts) into the
- * pieces that equal ranges of steps over the whole batch give; partials
+ * pieces that equal ranges of work over the whole batch give; partials
  * (normalised, rounded to bf16, with fp32 log-sum-exps) go to the handle's
  * workspace and are merged in fp32 by the log-sum-exp identity, in chunk
  * order: inside the attention kernel by the last chunk to finish when
