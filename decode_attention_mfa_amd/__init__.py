@@ -77,6 +77,8 @@ def _load_lib():
     lib.mfa_head_groups.restype = I32
     lib.mfa_debug_gather_kv.argtypes = [P, ctypes.POINTER(mfa_kv), I32, P, P, P]
     lib.mfa_debug_gather_kv.restype = ctypes.c_int
+    lib.mfa_debug_fp8_mfma.argtypes = [P, P, P, P, I32, P]
+    lib.mfa_debug_fp8_mfma.restype = ctypes.c_int
     lib.mfa_profile_enable.argtypes = [P, ctypes.c_int]
     lib.mfa_profile_enable.restype = ctypes.c_int
     lib.mfa_profile_read.argtypes = [P, P, P]
@@ -192,6 +194,13 @@ def mfa_head_groups(h: int, batch: int, max_seq_len: int = 0, min_seq_len: int =
 def mfa_debug_gather_kv(h: int, kv: mfa_kv, b: int, k_dst, v_dst, stream=None) -> None:
     _check(lib.mfa_debug_gather_kv(h, ctypes.byref(kv), b, _ptr(k_dst), _ptr(v_dst),
                                    _stream(stream)), "mfa_debug_gather_kv")
+
+
+def mfa_debug_fp8_mfma(a, b, c, d, n_tiles: int, stream=None) -> None:
+    """d = a . b + c per tile on the FP8 MFMA of the FP8-MFMA mode (a [n,16,128],
+    b [n,128,16] E4M3 codes; c (or None), d [n,16,16] fp32)."""
+    _check(lib.mfa_debug_fp8_mfma(_ptr(a), _ptr(b), _ptr(c), _ptr(d), n_tiles, _stream(stream)),
+           "mfa_debug_fp8_mfma")
 
 
 def mfa_profile_enable(h: int, enable: bool = True) -> None:

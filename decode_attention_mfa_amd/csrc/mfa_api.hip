@@ -529,6 +529,19 @@ int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, 
     return MFA_OK;
 }
 
+int mfa_debug_fp8_mfma(const void* a, const void* b, const float* c, float* d, int32_t n_tiles,
+                       void* hip_stream) {
+    g_last_error[0] = 0;
+    if (!a || !b || !d) return fail(MFA_ERR_INVALID, "mfa_debug_fp8_mfma: null a, b or d");
+    if (n_tiles < 0 || n_tiles > (1 << 20))
+        return fail(MFA_ERR_INVALID, "mfa_debug_fp8_mfma: n_tiles %d outside [0, 2^20]", n_tiles);
+    if (n_tiles == 0) return MFA_OK;
+    hipError_t e = mfa::launch_fp8_mfma((const uint8_t*)a, (const uint8_t*)b, c, d, n_tiles,
+                                        mfa::Launch{(hipStream_t)hip_stream});
+    if (e != hipSuccess) return hip_fail(e, "mfa_debug_fp8_mfma: launch");
+    return MFA_OK;
+}
+
 int mfa_profile_enable(mfa_handle h, int enable) {
     g_last_error[0] = 0;
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_profile_enable: not a live handle");

@@ -375,7 +375,14 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
         if (excl <= s_lo && s_lo < excl + cnt) {
             int P = excl;
             for (int bb = b0; bb < b1; bb++) {
-                const int len = per_t <= kRegLens ? lens[min(bb - b0, kRegLens - 1)] : seq_len(p.kv, bb);
+                int len;
+                if (per_t <= kRegLens) {   // lens[bb - b0], by selects (no indexed register array)
+                    len = lens[0];
+#pragma unroll
+                    for (int i = 1; i < kRegLens; i++) len = bb - b0 == i ? lens[i] : len;
+                } else {
+                    len = seq_len(p.kv, bb);
+                }
                 const int n = units_of_len(len);
                 if (s_lo < P + n) {
                     first_seq[0] = bb;
@@ -485,23 +492,58 @@ __global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
 }
 
 // Copy the logical rows t < L_b of sequence b through the attention kernel's
-// own address generation (kv_step_base). Block = one 64-token step.
+// own address generation (PieceRows, with the page indices of a piece held in
+// registers and read back per step). One wave per piece of kMaxPieceSteps
+// steps; it copies each step's rows 16 bytes per lane.
 template <bool PAGED>
-__global__ __launch_bounds__(256) void mfa_gather_kernel(const KvView kv, int b, uint8_t* k_dst,
-                                                         uint8_t* v_dst) {
+__global__ __launch_bounds__(64) void mfa_gather_kernel(const KvView kv, int b, uint8_t* k_dst, uint8_t* v_dst) {
     const int L = seq_len(kv, b);
-    const int t0 = blockIdx.x * kStep;
-    if (t0 >= L) return;
-    const int n = min(kStep, L - t0);
-    const int64_t base = kv_step_base<PAGED>(kv, b, t0);
+    const int t_begin = blockIdx.x * kMaxPieceSteps * kStep;
+    if (t_begin >= L) return;
+    const int l = threadIdx.x;
+    const int t_end = min(L, t_begin + kMaxPieceSteps * kStep);
+    const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
+    PieceRows<PAGED> rows;
+    rows.init(kv, b, t_begin, nsteps, l);
     const int per_row = kv.row_bytes / 16;
-    for (int i = threadIdx.x; i < n * per_row; i += blockDim.x) {
-        const int r = i / per_row, q = i - r * per_row;
-        const int64_t src = (base + r) * kv.row_bytes + 16 * q;
-        const int64_t dst = (int64_t)(t0 + r) * kv.row_bytes + 16 * q;
-        *reinterpret_cast<u32x4*>(k_dst + dst) = *reinterpret_cast<const u32x4*>(kv.k + src);
-        *reinterpret_cast<u32x4*>(v_dst + dst) = *reinterpret_cast<const u32x4*>(kv.v + src);
+    for (int s = 0; s < nsteps; s++) {
+        const int64_t base = rows.step_row(kv, 0, s);
+        const int t0 = t_begin + s * kStep;
+        const int n = min(kStep, L - t0);
+        for (int i = l; i < n * per_row; i += 64) {
+            const int r = i / per_row, q = i - r * per_row;
+            const int64_t src = (base + r) * kv.row_bytes + 16 * q;
+            const int64_t dst = (int64_t)(t0 + r) * kv.row_bytes + 16 * q;
+            *reinterpret_cast<u32x4*>(k_dst + dst) = *reinterpret_cast<const u32x4*>(kv.k + src);
+            *reinterpret_cast<u32x4*>(v_dst + dst) = *reinterpret_cast<const u32x4*>(kv.v + src);
+        }
     }
+}
+
+// One FP8 MFMA per tile, with the operand layout of the FP8-MFMA attention
+// mode (mfma16_fp8): a [n][16][128] and b [n][128][16] E4M3 codes, c and d
+// [n][16][16] fp32, row-major; lane l holds row l % 16 of A and column l % 16
+// of B over k = 32 (l / 16) .. + 31, and D rows 4 (l / 16) .. + 3 of column
+// l % 16.
+__global__ __launch_bounds__(64) void mfa_fp8_mfma_kernel(const uint8_t* a, const uint8_t* b, const float* c,
+                                                           float* d) {
+    const int64_t t = blockIdx.x;
+    const int l = threadIdx.x, r = l & 15, kq = l >> 4;
+    const uint8_t* at = a + t * 16 * 128 + r * 128 + 32 * kq;
+    const uint8_t* bt = b + t * 128 * 16 + (32 * kq) * 16 + r;
+    i32x8 av, bv;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        av[j] = *reinterpret_cast<const int*>(at + 4 * j);
+        bv[j] = (int)((uint32_t)bt[(4 * j) * 16] | ((uint32_t)bt[(4 * j + 1) * 16] << 8) |
+                      ((uint32_t)bt[(4 * j + 2) * 16] << 16) | ((uint32_t)bt[(4 * j + 3) * 16] << 24));
+    }
+    f32x4 acc;
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i] = c ? c[t * 256 + (4 * kq + i) * 16 + r] : 0.f;
+    acc = mfma16_fp8(av, bv, acc);
+#pragma unroll
+    for (int i = 0; i < 4; i++) d[t * 256 + (4 * kq + i) * 16 + r] = acc[i];
 }
 
 hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l) {
@@ -549,10 +591,15 @@ hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l) {
 
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
                          void* v_dst, const Launch& l) {
-    const int nblk = (max_seq_len + kStep - 1) / kStep;
+    const int nblk = (max_seq_len + kMaxPieceSteps * kStep - 1) / (kMaxPieceSteps * kStep);
     if (nblk == 0) return hipSuccess;
-    return launch_kernel(paged ? mfa_gather_kernel<true> : mfa_gather_kernel<false>, dim3(nblk), dim3(256), l, kv,
+    return launch_kernel(paged ? mfa_gather_kernel<true> : mfa_gather_kernel<false>, dim3(nblk), dim3(64), l, kv,
                          b, (uint8_t*)k_dst, (uint8_t*)v_dst);
+}
+
+hipError_t launch_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d, int n_tiles,
+                           const Launch& l) {
+    return launch_kernel(mfa_fp8_mfma_kernel, dim3(n_tiles), dim3(64), l, a, b, c, d);
 }
 
 }  // namespace mfa

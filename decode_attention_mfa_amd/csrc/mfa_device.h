@@ -1,8 +1,9 @@
 // mfa_device.h -- device-side helpers shared by the MFA kernels (gfx950).
 //
 // Vector types for the CDNA4 matrix cores, FP8 E4M3 -> bf16 conversion in
-// registers, and the KV-cache address generation used by both the attention
-// kernel and the debug gather (so that the two follow one code path).
+// registers, and the KV-cache address generation (PieceRows) that both the
+// attention kernel and the debug gather use, so that the paging test checks
+// the attention kernel's own addressing.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,6 +12,7 @@
 namespace mfa {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -73,6 +75,11 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
     return bitcast<bf16x8>(u32x4{a.x, a.y, b.x, b.y});
 }
 
+// Larger of two floats by the IEEE maximum operation (a NaN input gives NaN):
+// gfx950 has it in a three-input form, and unlike fmaxf it needs no quieting
+// of its inputs first.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     bf16x2 v = {(__bf16)a, (__bf16)b};  // round to nearest even
     return bitcast<uint32_t>(v);
@@ -132,5 +139,38 @@ __device__ __forceinline__ int64_t kv_group_step_base(const KvView& kv, int b, i
         return ((int64_t)b * kv.groups + g) * kv.kv_stride + t0;
     }
 }
+
+// The rows of the 64-token steps of one piece (tokens [t_begin, ...) of
+// sequence b, t_begin a multiple of 64, at most kMaxPieceSteps steps), as the
+// attention kernel and the debug gather address them. For a paged cache lane
+// j of the wave holds the page of step j (pg0) and of step 64 + j (pg1),
+// loaded once; a step reads its page back with v_readlane, so no page-table
+// load sits in a step loop. Step s covers rows step_row(s) .. step_row(s)+63
+// of K/V head g.
+constexpr int kMaxPieceSteps = 128;
+template <bool PAGED>
+struct PieceRows {
+    int32_t pg0 = 0, pg1 = 0;
+    int32_t b = 0, t_begin = 0;
+
+    __device__ __forceinline__ void init(const KvView& kv, int b_, int t_begin_, int nsteps, int lane) {
+        b = b_;
+        t_begin = t_begin_;
+        if constexpr (PAGED) {
+            const int32_t* pt = kv.page_table + (int64_t)b * kv.pt_stride + (t_begin >> 6);
+            if (lane < nsteps) pg0 = pt[lane];
+            if (64 + lane < nsteps) pg1 = pt[64 + lane];
+        }
+    }
+    // s must be wave-uniform
+    __device__ __forceinline__ int64_t step_row(const KvView& kv, int g, int s) const {
+        if constexpr (PAGED) {
+            const int32_t page = s < 64 ? __builtin_amdgcn_readlane(pg0, s) : __builtin_amdgcn_readlane(pg1, s - 64);
+            return ((int64_t)page * kv.groups + g) * kPage;
+        } else {
+            return kv_group_step_base<false>(kv, b, g, t_begin + s * kStep);
+        }
+    }
+};
 
 }  // namespace mfa

@@ -70,12 +70,16 @@ constexpr int kFusedMaxChunks = 2;
 
 // Paged caches: at most this many 64-token steps per split chunk (the
 // attention kernel keeps a chunk's page indices in two registers per lane).
-constexpr int kMaxPagedChunkSteps = 128;
+constexpr int kMaxPagedChunkSteps = kMaxPieceSteps;
 
 hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l);
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l);
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
                          void* v_dst, const Launch& l);
+// n_tiles FP8 MFMAs (16 x 16 x 128, E4M3 operands) as the FP8-MFMA attention
+// mode runs them: d = a . b + c per tile (c may be null: zero)
+hipError_t launch_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d, int n_tiles,
+                           const Launch& l);
 
 struct QprojArgs {
     const uint16_t* x;      // [B][hidden]

@@ -240,9 +240,20 @@ int32_t mfa_head_groups(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_
 
 /* Test support: copy the logical K and V rows t < L_b of sequence b into
  * contiguous device buffers k_dst, v_dst ([max_seq_len][256] elements of the
- * cache type) with the same address generation mfa_decode uses. */
+ * cache type) with the attention kernel's own address generation (for a paged
+ * cache: the page indices of a piece of up to 128 steps held in registers and
+ * read back per 64-token step). The page table is trusted as in mfa_decode. */
 int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, void* v_dst,
                         void* hip_stream);
+
+/* Test support: the FP8 matrix operation of the MFA_ATTN_FP8_MFMA mode on
+ * given operands, so that its arithmetic can be measured: for each of n_tiles
+ * tiles, d = a . b + c with a [16][128] and b [128][16] OCP E4M3 codes and c,
+ * d [16][16] fp32, all row-major and contiguous per tile (a, b, c, d device
+ * pointers; c may be NULL for zero). No handle; 0 <= n_tiles <= 2^20.
+ * Asynchronous on hip_stream. */
+int mfa_debug_fp8_mfma(const void* a, const void* b, const float* c, float* d, int32_t n_tiles,
+                       void* hip_stream);
 
 /* Kernel kinds reported by mfa_profile_read. */
 enum mfa_kernel_kind {

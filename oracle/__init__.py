@@ -67,6 +67,10 @@ def _load():
         lib.oracle_attention_grouped.argtypes = [I, I, I, I, P, I, P, P, D, D, P, P, I, I, I64, D, I,
                                                  P, P, I]
         lib.oracle_attention_grouped.restype = I
+        lib.oracle_attention_fp8mma.argtypes = [I, I, I, P, P, P, D, D, P, P, I, I, I64, D, P, P, I]
+        lib.oracle_attention_fp8mma.restype = I
+        lib.oracle_fp8_q_exponent.argtypes = [D]
+        lib.oracle_fp8_q_exponent.restype = I
         lib.oracle_weights.argtypes = [I, I, P, I, I, I, P, D, P, P, I, I, I64, D, P]
         lib.oracle_weights.restype = I
         lib.oracle_gather_kv.argtypes = [I, I, I, P, P, P, P, I, I, I64, P, P]
@@ -233,6 +237,41 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, *, kv_dtype
     return o, lse
 
 
+def fp8_q_exponent(amax: float) -> int:
+    """The power of two 2^e that puts a head's largest |q| in [128, 256)
+    (e = 0 for an all-zero head, e limited to [-100, 100])."""
+    return int(_load().oracle_fp8_q_exponent(float(amax)))
+
+
+def attention_fp8mma(q_bits: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, *, k_scale: float = 1.0,
+                     v_scale: float = 1.0, page_table=None, page_size: int = 64,
+                     softmax_scale: float = 1.0 / 16.0, nthreads: int = 0):
+    """Attention in FP8 arithmetic (E4M3 query per head with a power-of-two
+    scale, E4M3 weights 4P against an integer reference, applied-weight
+    normalisation; see oracle_attention_fp8mma in the C file). q_bits [B, H, D]
+    bf16 bits; k, v E4M3 codes, contiguous [B, S, D] or paged [P, page, D].
+    Returns (o [B, H, D], lse [B, H]) fp64."""
+    q_bits = _c(q_bits, np.uint16)
+    B, H, D = q_bits.shape
+    k = _c(k, np.uint8)
+    v = _c(v, np.uint8)
+    L = _c(seq_lens, np.int32)
+    assert L.shape == (B,) and k.shape == v.shape and k.shape[-1] == D and k.ndim == 3
+    if page_table is not None:
+        pt = _c(page_table, np.int32)
+        pt_stride, kv_stride, page_size = pt.shape[1], 0, k.shape[1]
+    else:
+        pt, pt_stride, kv_stride = None, 0, k.shape[1]
+    o = np.empty((B, H, D), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    rc = _load().oracle_attention_fp8mma(B, H, D, _ptr(q_bits), _ptr(k), _ptr(v), float(k_scale),
+                                         float(v_scale), _ptr(L), _ptr(pt), pt_stride, page_size, kv_stride,
+                                         float(softmax_scale), _ptr(o), _ptr(lse), nthreads)
+    if rc:
+        raise RuntimeError(f"oracle_attention_fp8mma failed: {rc}")
+    return o, lse
+
+
 def attention_mtp(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, *, kv_dtype: int,
                   k_scale: float = 1.0, v_scale: float = 1.0, page_table=None, page_size: int = 64,
                   softmax_scale: float = 1.0 / 16.0, nthreads: int = 0):
@@ -299,6 +338,15 @@ def case_q(case) -> np.ndarray:
         return decode_bf16(case.q)
     q = qproj(case.x, case.w_qa, case.gamma, case.w_qb, eps=case.rms_eps)
     return q.reshape(case.batch, NUM_HEADS, HEAD_DIM)
+
+
+def case_attention_fp8mma(case, nthreads: int = 0):
+    """Oracle output (o, lse) of a ``synth.Case`` with an FP8 cache in the FP8
+    attention arithmetic (its Q is the given bf16 Q)."""
+    assert case.kv_dtype == "fp8" and case.q is not None
+    return attention_fp8mma(case.q, case.k, case.v, case.seq_lens, k_scale=case.k_scale,
+                            v_scale=case.v_scale, page_table=case.page_table,
+                            softmax_scale=case.softmax_scale, nthreads=nthreads)
 
 
 def case_attention(case, q: Optional[np.ndarray] = None, chunk: int = 0, nthreads: int = 0):

@@ -395,6 +395,145 @@ int oracle_attention(int B, int H, int D, const double* q, int kv_dtype,
                                     chunk, o, lse, nthreads);
 }
 
+/* ------------------------------------------------- FP8 attention arithmetic */
+/*
+ * Attention computed in FP8, the precision the Step-3 summary card's Key
+ * points give for its decoding throughput (4K context, FP8; a BF16-attention
+ * ablation is slower). The pages do not say how the query and the softmax
+ * weights are quantised; the reading taken here:
+ *
+ *   1. each head's query q (bf16 values) is scaled by 2^e, the power of two
+ *      that puts its largest |q_d| in [128, 256): e = 7 - floor(log2 max|q|),
+ *      limited to [-100, 100] (e = 0 for an all-zero head); every q_d * 2^e
+ *      is rounded (as a float) to E4M3 by round-to-nearest-even, giving q8;
+ *   2. scores are exact dot products of q8 with the cached key codes, in
+ *      base 2: s2_t = <q8, k_t> * softmax_scale * k_scale * log2(e) * 2^-e;
+ *   3. the weights are taken against an integer reference r = ceil(max_t
+ *      s2_t): P_t = 2^(s2_t - r) lies in (0, 1], and 4 P_t is rounded (as a
+ *      float) to E4M3 by round-to-nearest-even, subnormal codes included;
+ *      p8_t is that E4M3 value divided by 4;
+ *   4. o = v_scale * sum_t p8_t v_t / S8 with S8 = sum_t p8_t (the weights
+ *      applied to V sum to one), and lse = ln(2) * (r + log2 S8).
+ *
+ * Because r is an integer, E4M3's normal range makes p8 independent of which
+ * integer reference is used (a power of two scales every code exactly), so
+ * the result does not depend on how the context is cut into pieces, except
+ * for weights whose 4 P falls below E4M3's smallest normal value (2^-6).
+ * With E4M3 replaced by exact arithmetic (inputs whose q * 2^e and 4 P are
+ * E4M3 values) this is plain softmax attention, oracle_attention.
+ *
+ * q is given as bf16 bits [B][H][D]; k and v are E4M3 codes, contiguous
+ * [B][kv_stride][D] or paged [P][page_size][D]. Outputs o [B][H][D] and lse
+ * [B][H] (NULL allowed); an empty sequence gives o = 0 and lse = -inf.
+ */
+uint8_t oracle_f32_to_e4m3(float x);   /* defined with the KV append below */
+
+static double e4m3_round_f32(double x) {
+    return g_e4m3[oracle_f32_to_e4m3((float)x)];
+}
+
+/* The exponent e of step 1 for a head whose largest |q_d| is amax. */
+int oracle_fp8_q_exponent(double amax) {
+    if (!(amax > 0.0))
+        return 0;
+    int x;
+    (void)frexp(amax, &x);              /* amax = f * 2^x, f in [0.5, 1) */
+    int e = 7 - (x - 1);                /* floor(log2 amax) = x - 1 */
+    if (e > 100)
+        e = 100;
+    if (e < -100)
+        e = -100;
+    return e;
+}
+
+int oracle_attention_fp8mma(int B, int H, int D, const uint16_t* q, const uint8_t* k,
+                            const uint8_t* v, double k_scale, double v_scale,
+                            const int32_t* seq_lens, const int32_t* page_table, int pt_stride,
+                            int page_size, int64_t kv_stride, double softmax_scale,
+                            double* o, double* lse, int nthreads) {
+    int rc = check_args(B, H, D, seq_lens, page_size, page_table, pt_stride, kv_stride);
+    if (rc)
+        return rc;
+    e4m3_table_init();
+    set_threads(nthreads);
+    const kv_view kv = {OR_FP8_E4M3, k, v, 1.0, 1.0, page_table, pt_stride, page_size,
+                        kv_stride, D, 1, 0};
+    const double log2e = 1.0 / log(2.0);
+    int maxL = 0;
+    for (int b = 0; b < B; b++)
+        if (seq_lens[b] > maxL)
+            maxL = seq_lens[b];
+    int failed = 0;
+    #pragma omp parallel
+    {
+        double* s2 = (double*)malloc(((size_t)maxL + 1) * sizeof(double));
+        double* q8 = (double*)malloc((size_t)D * sizeof(double));
+        if (!s2 || !q8) {
+            #pragma omp atomic write
+            failed = 1;
+        }
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < (int64_t)B * H; bh++) {
+            if (failed)
+                continue;
+            int b = (int)(bh / H);
+            int L = seq_lens[b];
+            double* ov = o + (size_t)bh * D;
+            for (int d = 0; d < D; d++)
+                ov[d] = 0.0;
+            if (L == 0) {
+                if (lse)
+                    lse[bh] = -INFINITY;
+                continue;
+            }
+            /* step 1: per-head power-of-two scale, E4M3 query */
+            const uint16_t* qh = q + (size_t)bh * D;
+            double amax = 0.0;
+            for (int d = 0; d < D; d++) {
+                double a = fabs(oracle_bf16_to_f64(qh[d]));
+                if (a > amax)
+                    amax = a;
+            }
+            int e = oracle_fp8_q_exponent(amax);
+            for (int d = 0; d < D; d++)
+                q8[d] = e4m3_round_f32(ldexp(oracle_bf16_to_f64(qh[d]), e));
+            /* step 2: exact scores, base 2 */
+            double sc = softmax_scale * k_scale * log2e * ldexp(1.0, -e);
+            for (int t = 0; t < L; t++) {
+                int64_t row = kv_row(&kv, b, t);
+                double dot = 0.0;
+                for (int d = 0; d < D; d++)
+                    dot += q8[d] * g_e4m3[k[(size_t)row * D + d]];
+                s2[t] = dot * sc;
+            }
+            /* step 3: weights against the integer reference, E4M3 of 4 P */
+            double M = -INFINITY;
+            for (int t = 0; t < L; t++)
+                if (s2[t] > M)
+                    M = s2[t];
+            double r = ceil(M);
+            double S8 = 0.0;
+            for (int t = 0; t < L; t++) {
+                s2[t] = e4m3_round_f32(4.0 * exp2(s2[t] - r)) / 4.0;   /* p8_t, in place */
+                S8 += s2[t];
+            }
+            /* step 4: weighted V, normalised by the sum of the applied weights */
+            for (int t = 0; t < L; t++) {
+                int64_t row = kv_row(&kv, b, t);
+                for (int d = 0; d < D; d++)
+                    ov[d] += s2[t] * g_e4m3[v[(size_t)row * D + d]];
+            }
+            for (int d = 0; d < D; d++)
+                ov[d] = ov[d] * v_scale / S8;
+            if (lse)
+                lse[bh] = log(2.0) * r + log(S8);
+        }
+        free(s2);
+        free(q8);
+    }
+    return failed ? -3 : 0;
+}
+
 /* Softmax weights of one (b, h) over all L_b tokens, in token order:
  * w[t] = exp(s_t - M) / sum_u exp(s_u - M). For the sum-to-one pin. */
 int oracle_weights(int H, int D, const double* q, int b, int h, int kv_dtype,

@@ -75,6 +75,8 @@ def test_null_arguments_are_rejected():
     assert "handle" in m.mfa_last_error()
     assert m.lib.mfa_qproj(None, None, None, None, None, None, 1, None) == m.MFA_ERR_INVALID
     assert m.lib.mfa_debug_gather_kv(None, ctypes.byref(kv), 0, None, None, None) == m.MFA_ERR_INVALID
+    assert m.lib.mfa_debug_fp8_mfma(None, None, None, None, 1, None) == m.MFA_ERR_INVALID
+    assert m.lib.mfa_debug_fp8_mfma(1, 1, None, 1, -1, None) == m.MFA_ERR_INVALID
     assert m.lib.mfa_kv_append(None, None, None, None, ctypes.byref(kv), 1, None) == m.MFA_ERR_INVALID
     assert "handle" in m.mfa_last_error()
     assert m.lib.mfa_destroy(None) == m.MFA_OK

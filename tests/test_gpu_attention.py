@@ -168,10 +168,14 @@ def test_paged_equals_contiguous_bitwise():
             assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_debug_gather_bit_exact():
+@pytest.mark.parametrize("paged", [True, False])
+def test_debug_gather_bit_exact(paged):
+    """The page-table gather, bit for bit, through the attention kernel's own
+    addressing (page indices of a piece of up to 128 steps in registers):
+    lengths with partial pages and more than one such piece."""
     m, hz = _mfa()
     for kv in ("fp8", "bf16"):
-        pc = synth.make_case("g", 5, [1, 63, 64, 200, 511], kv, seed=80, paged=True)
+        pc = synth.make_case("g", 8, [1, 63, 64, 200, 511, 8192, 8193, 20000], kv, seed=80, paged=paged)
         dc = hz.to_device(pc)
         h = hz.create_handle(dc)
         try:
