@@ -71,6 +71,8 @@ def _load_lib():
     lib.mfa_kv_append.argtypes = [P, P, P, P, ctypes.POINTER(mfa_kv), I32, P]
     lib.mfa_kv_append.restype = ctypes.c_int
     lib.mfa_decode.restype = ctypes.c_int
+    lib.mfa_decode_noalloc.argtypes = [ctypes.POINTER(mfa_config), P, ctypes.POINTER(mfa_kv), P, P, I32, P]
+    lib.mfa_decode_noalloc.restype = ctypes.c_int
     lib.mfa_split_tokens.argtypes = [P, I32, I32, I32]
     lib.mfa_split_tokens.restype = I32
     lib.mfa_head_groups.argtypes = [P, I32, I32, I32]
@@ -169,6 +171,13 @@ def mfa_qproj(h: int, x, w_qa, rms_w, w_qb, q_out, batch: int, stream=None) -> N
 def mfa_decode(h: int, q, kv: mfa_kv, out, lse_out, batch: int, stream=None) -> None:
     _check(lib.mfa_decode(h, _ptr(q), ctypes.byref(kv), _ptr(out), _ptr(lse_out), batch,
                           _stream(stream)), "mfa_decode")
+
+
+def mfa_decode_noalloc(cfg: mfa_config, q, kv: mfa_kv, out, lse_out, batch: int, stream=None) -> None:
+    """mfa_decode without a handle: the library's static device workspace
+    (allocates nothing)."""
+    _check(lib.mfa_decode_noalloc(ctypes.byref(cfg), _ptr(q), ctypes.byref(kv), _ptr(out), _ptr(lse_out), batch,
+                                  _stream(stream)), "mfa_decode_noalloc")
 
 
 def mfa_decode_mtp(h: int, q, kv: mfa_kv, num_tokens: int, out, lse_out, batch: int, stream=None) -> None:

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -36,6 +37,32 @@ constexpr int kMaxAutoSplit = 2048;
 
 }  // namespace
 
+// ---------------------------------------------------------------- scratch
+// Device workspace of mfa_decode_noalloc, for callers that cannot allocate:
+// a file-scope array that every GPU the library runs on holds until the
+// process ends. The first kNoAllocCounterBytes hold the arrival counters
+// (zero between calls: cleared once per device, and every kernel that counts
+// resets what it used); the rest holds the chunk partials. Host code uses
+// the array only through the per-device address taken once with
+// hipGetSymbolAddress (its name on the host is not a device address).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr size_t kNoAllocCounterBytes = size_t(1) << 20;   // [max_batch <= 65536][4] int32
+// partial slots (a [64][256] bf16 row block and 64 fp32 log-sum-exps each)
+constexpr int64_t kSlotBytes = 64 * 256 * 2 + 64 * 4;
+constexpr int64_t kNoAllocSlots = (int64_t)(kNoAllocScratchBytes - kNoAllocCounterBytes) / kSlotBytes;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    uint8_t* ptr = nullptr;   // device address of `scratch` on this device
+    int num_cu = 0;
+    bool cleared = false;     // the counter region's clear has been enqueued
+};
+std::mutex g_scratch_mutex;
+ScratchSlot g_scratch[kMaxDevices];
+}  // namespace
+
 // Optional per-kernel timing: a ring of hipEvent pairs, each pair stamped
 // with one kernel's start and end by the launch itself.
 struct Profiler {
@@ -53,6 +80,7 @@ struct mfa_ctx {
     int device;
     int num_cu;
     int max_chunks;        // per sequence, at the smallest chunk this handle may use
+    int64_t part_slots;    // partial slots the workspace holds
     float* part_o;         // [max_batch * max_chunks][64][256] bf16
     float* part_lse;       // [max_batch * max_chunks][64]
     int32_t* counters;     // [max_batch][2], zero between calls
@@ -171,51 +199,69 @@ const char* mfa_status_string(int status) {
 
 const char* mfa_last_error(void) { return g_last_error; }
 
+// Checks a configuration and fills in its defaults (kv_heads 0 -> 1); fn
+// names the entry point in the error message.
+static int validate_config(const mfa_config* cfg, mfa_config* out, const char* fn) {
+    mfa_config c = *cfg;
+    if (c.num_heads != mfa::kHeads || c.head_dim != mfa::kHeadDim)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: only 64 heads x 256 are supported (got %d x %d)", fn,
+                    c.num_heads, c.head_dim);
+    if (c.hidden <= 0 || c.hidden % mfa::kQprojRowsPerSplit != 0)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: hidden must be a positive multiple of %d (got %d)", fn,
+                    mfa::kQprojRowsPerSplit, c.hidden);
+    if (c.q_rank <= 0 || c.q_rank % 64 != 0 || c.q_rank > 64 * mfa::kMaxNormBlocks)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: q_rank must be a positive multiple of 64, at most %d (got %d)", fn,
+                    64 * mfa::kMaxNormBlocks, c.q_rank);
+    if (c.kv_dtype != MFA_DTYPE_BF16 && c.kv_dtype != MFA_DTYPE_FP8_E4M3)
+        return fail(MFA_ERR_INVALID, "%s: bad kv_dtype %d", fn, c.kv_dtype);
+    if (c.page_size != 0 && c.page_size != mfa::kPage)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: page_size must be 0 or 64 (got %d)", fn, c.page_size);
+    if (c.max_batch < 1 || c.max_context < 1)
+        return fail(MFA_ERR_INVALID, "%s: max_batch and max_context must be >= 1", fn);
+    if (c.split_tokens < MFA_SPLIT_BALANCED || (c.split_tokens > 0 && c.split_tokens % mfa::kStep != 0))
+        return fail(MFA_ERR_INVALID,
+                    "%s: split_tokens must be 0, MFA_SPLIT_BALANCED or a positive multiple of 64 (got %d)", fn,
+                    c.split_tokens);
+    if (c.page_size != 0 && c.split_tokens > mfa::kMaxPagedChunkSteps * mfa::kStep)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: with a paged cache split_tokens must be <= %d (got %d)", fn,
+                    mfa::kMaxPagedChunkSteps * mfa::kStep, c.split_tokens);
+    if (!(c.softmax_scale > 0.f) || !isfinite(c.softmax_scale))
+        return fail(MFA_ERR_INVALID, "%s: softmax_scale must be finite and > 0", fn);
+    if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))
+        return fail(MFA_ERR_INVALID, "%s: rms_eps must be finite and >= 0", fn);
+    if (c.attn_math != MFA_ATTN_BF16_MFMA && c.attn_math != MFA_ATTN_FP8_MFMA)
+        return fail(MFA_ERR_INVALID, "%s: bad attn_math %d", fn, c.attn_math);
+    if (c.attn_math == MFA_ATTN_FP8_MFMA && c.kv_dtype != MFA_DTYPE_FP8_E4M3)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: attn_math FP8_MFMA needs an FP8 cache", fn);
+    if (c.kv_heads == 0) c.kv_heads = 1;
+    if (c.kv_heads != 1 && c.kv_heads != 2 && c.kv_heads != 4)
+        return fail(MFA_ERR_INVALID, "%s: kv_heads must be 1, 2 or 4 (got %d)", fn, c.kv_heads);
+    if (c.kv_heads > 1 && (c.kv_dtype != MFA_DTYPE_FP8_E4M3 || c.attn_math != MFA_ATTN_BF16_MFMA ||
+                           c.split_tokens == MFA_SPLIT_BALANCED))
+        return fail(MFA_ERR_UNSUPPORTED,
+                    "%s: kv_heads > 1 needs an FP8 cache, MFA_ATTN_BF16_MFMA and chunked splits", fn);
+
+    *out = c;
+    return MFA_OK;
+}
+
+// Chunks per sequence at the smallest chunk the configuration allows (the
+// workspace holds one more partial slot per sequence: a balanced split may
+// cut a sequence into ceil(steps / 4) + 1 pieces).
+static int64_t workspace_chunks(const mfa_config& c) {
+    const int min_chunk = c.split_tokens > 0 ? c.split_tokens : kMinAutoSplit;
+    return ((int64_t)c.max_context + min_chunk - 1) / min_chunk;
+}
+
 int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     g_last_error[0] = 0;
     if (!cfg || !out) return fail(MFA_ERR_INVALID, "mfa_create: null cfg or out");
     *out = nullptr;
-    mfa_config c = *cfg;
-    if (c.num_heads != mfa::kHeads || c.head_dim != mfa::kHeadDim)
-        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: only 64 heads x 256 are supported (got %d x %d)",
-                    c.num_heads, c.head_dim);
-    if (c.hidden <= 0 || c.hidden % mfa::kQprojRowsPerSplit != 0)
-        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: hidden must be a positive multiple of %d (got %d)",
-                    mfa::kQprojRowsPerSplit, c.hidden);
-    if (c.q_rank <= 0 || c.q_rank % 64 != 0 || c.q_rank > 64 * mfa::kMaxNormBlocks)
-        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: q_rank must be a positive multiple of 64, at most %d (got %d)",
-                    64 * mfa::kMaxNormBlocks, c.q_rank);
-    if (c.kv_dtype != MFA_DTYPE_BF16 && c.kv_dtype != MFA_DTYPE_FP8_E4M3)
-        return fail(MFA_ERR_INVALID, "mfa_create: bad kv_dtype %d", c.kv_dtype);
-    if (c.page_size != 0 && c.page_size != mfa::kPage)
-        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: page_size must be 0 or 64 (got %d)", c.page_size);
-    if (c.max_batch < 1 || c.max_context < 1)
-        return fail(MFA_ERR_INVALID, "mfa_create: max_batch and max_context must be >= 1");
-    if (c.split_tokens < MFA_SPLIT_BALANCED || (c.split_tokens > 0 && c.split_tokens % mfa::kStep != 0))
-        return fail(MFA_ERR_INVALID,
-                    "mfa_create: split_tokens must be 0, MFA_SPLIT_BALANCED or a positive multiple of 64 (got %d)",
-                    c.split_tokens);
-    if (c.page_size != 0 && c.split_tokens > mfa::kMaxPagedChunkSteps * mfa::kStep)
-        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: with a paged cache split_tokens must be <= %d (got %d)",
-                    mfa::kMaxPagedChunkSteps * mfa::kStep, c.split_tokens);
-    if (!(c.softmax_scale > 0.f) || !isfinite(c.softmax_scale))
-        return fail(MFA_ERR_INVALID, "mfa_create: softmax_scale must be finite and > 0");
-    if (!(c.rms_eps >= 0.f) || !isfinite(c.rms_eps))
-        return fail(MFA_ERR_INVALID, "mfa_create: rms_eps must be finite and >= 0");
-    if (c.attn_math != MFA_ATTN_BF16_MFMA && c.attn_math != MFA_ATTN_FP8_MFMA)
-        return fail(MFA_ERR_INVALID, "mfa_create: bad attn_math %d", c.attn_math);
-    if (c.attn_math == MFA_ATTN_FP8_MFMA && c.kv_dtype != MFA_DTYPE_FP8_E4M3)
-        return fail(MFA_ERR_UNSUPPORTED, "mfa_create: attn_math FP8_MFMA needs an FP8 cache");
-    if (c.kv_heads == 0) c.kv_heads = 1;
-    if (c.kv_heads != 1 && c.kv_heads != 2 && c.kv_heads != 4)
-        return fail(MFA_ERR_INVALID, "mfa_create: kv_heads must be 1, 2 or 4 (got %d)", c.kv_heads);
-    if (c.kv_heads > 1 && (c.kv_dtype != MFA_DTYPE_FP8_E4M3 || c.attn_math != MFA_ATTN_BF16_MFMA ||
-                           c.split_tokens == MFA_SPLIT_BALANCED))
-        return fail(MFA_ERR_UNSUPPORTED,
-                    "mfa_create: kv_heads > 1 needs an FP8 cache, MFA_ATTN_BF16_MFMA and chunked splits");
+    mfa_config c;
+    int rc = validate_config(cfg, &c, "mfa_create");
+    if (rc) return rc;
 
-    const int min_chunk = c.split_tokens > 0 ? c.split_tokens : kMinAutoSplit;
-    const int64_t max_chunks = ((int64_t)c.max_context + min_chunk - 1) / min_chunk;
+    const int64_t max_chunks = workspace_chunks(c);
     // one more slot per sequence than chunks: a balanced split may cut a
     // sequence into ceil(steps / 4) + 1 pieces
     const int64_t nparts = (int64_t)c.max_batch * (max_chunks + 1);
@@ -233,6 +279,7 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     if (!h) return fail(MFA_ERR_NOMEM, "mfa_create: host allocation failed");
     h->cfg = c;
     h->max_chunks = (int)max_chunks;
+    h->part_slots = nparts;
     hipError_t e = hipGetDevice(&h->device);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device);
     if (e != hipSuccess) {
@@ -450,6 +497,9 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
         const int reps = qtok * a.nh;
         workgroups = reps == 1 ? batch * a.n_chunk : round_up((int64_t)batch * a.n_chunk, 8) * reps;
     }
+    if ((int64_t)rows * a.part_stride > h->part_slots)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: %d query rows x %d partial slots exceed the workspace's %lld", fn, rows,
+                    a.part_stride, (long long)h->part_slots);
     const float log2e = 1.4426950408889634f;
     a.score_scale = h->cfg.softmax_scale * (fp8 ? kv->k_scale : 1.0f) * log2e;
     a.v_scale = fp8 ? kv->v_scale : 1.0f;
@@ -473,6 +523,71 @@ int mfa_decode_mtp(mfa_handle h, const void* q, const mfa_kv* kv, int32_t num_to
                    int32_t batch, void* hip_stream) {
     g_last_error[0] = 0;
     return decode_impl(h, q, kv, num_tokens, out, lse_out, batch, hip_stream, "mfa_decode_mtp");
+}
+
+// The workspace of mfa_decode_noalloc on the current device: the address of
+// `scratch` there, taken once per device with the device current, and the
+// compute-unit count; the counter region is cleared by a fill kernel on the
+// first call's stream (a kernel, not a memset, so that the call may be
+// captured in a graph).
+static int noalloc_setup(hipStream_t st, ScratchSlot* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "mfa_decode_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_decode_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ScratchSlot& sl = g_scratch[dev];
+    if (!sl.ptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e, "mfa_decode_noalloc: hipGetSymbolAddress(scratch)");
+        int ncu = 0;
+        e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "mfa_decode_noalloc: device query");
+        sl.ptr = (uint8_t*)p;
+        sl.num_cu = ncu;
+    }
+    if (!sl.cleared) {
+        e = mfa::launch_fill_zero((uint32_t*)sl.ptr, kNoAllocCounterBytes / 4, mfa::Launch{st});
+        if (e != hipSuccess) return hip_fail(e, "mfa_decode_noalloc: clearing the counters");
+        sl.cleared = true;
+    }
+    *out = sl;
+    return MFA_OK;
+}
+
+int mfa_decode_noalloc(const mfa_config* cfg, const void* q, const mfa_kv* kv, void* out, float* lse_out,
+                       int32_t batch, void* hip_stream) {
+    g_last_error[0] = 0;
+    if (!cfg) return fail(MFA_ERR_INVALID, "mfa_decode_noalloc: null cfg");
+    mfa_config c;
+    int rc = validate_config(cfg, &c, "mfa_decode_noalloc");
+    if (rc) return rc;
+    if ((int64_t)c.max_batch * 4 * 4 > (int64_t)kNoAllocCounterBytes)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_decode_noalloc: max_batch %d exceeds the scratch's %d", c.max_batch,
+                    (int)(kNoAllocCounterBytes / 16));
+    hipStream_t st = (hipStream_t)hip_stream;
+    ScratchSlot sl;
+    rc = noalloc_setup(st, &sl);
+    if (rc) return rc;
+    // a handle on the stack: the kernels see the same arguments as through
+    // mfa_create, with the workspace in the scratch (counters first, then
+    // kNoAllocSlots partial row blocks, then their log-sum-exps); the call's
+    // split is checked against kNoAllocSlots in decode_impl
+    mfa_ctx h{};
+    h.magic = kMagic;
+    h.cfg = c;
+    h.num_cu = sl.num_cu;
+    (void)hipGetDevice(&h.device);
+    h.max_chunks = (int)workspace_chunks(c);
+    h.part_slots = kNoAllocSlots;
+    h.counters = (int32_t*)sl.ptr;
+    h.part_o = (float*)(sl.ptr + kNoAllocCounterBytes);
+    h.part_lse = (float*)(sl.ptr + kNoAllocCounterBytes + kNoAllocSlots * mfa::kHeads * mfa::kHeadDim * 2);
+    rc = decode_impl(&h, q, kv, 1, out, lse_out, batch, hip_stream, "mfa_decode_noalloc");
+    h.magic = kDead;
+    return rc;
 }
 
 int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v, const mfa_kv* kv,

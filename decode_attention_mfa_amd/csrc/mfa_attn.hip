@@ -37,6 +37,7 @@
 // of the sequence's pieces to finish (balanced launches, and chunked launches
 // where no sequence has more than two chunks), or by mfa_combine_kernel
 // afterwards.
+#include <algorithm>
 #include <type_traits>
 
 #include "mfa_device.h"
@@ -595,6 +596,16 @@ hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, v
     if (nblk == 0) return hipSuccess;
     return launch_kernel(paged ? mfa_gather_kernel<true> : mfa_gather_kernel<false>, dim3(nblk), dim3(64), l, kv,
                          b, (uint8_t*)k_dst, (uint8_t*)v_dst);
+}
+
+__global__ __launch_bounds__(256) void mfa_fill_zero_kernel(uint32_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0;
+}
+
+hipError_t launch_fill_zero(uint32_t* p, size_t n, const Launch& l) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = std::min<size_t>((n + 255) / 256, 1024);
+    return launch_kernel(mfa_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), l, p, n);
 }
 
 hipError_t launch_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d, int n_tiles,

@@ -76,6 +76,9 @@ hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgr
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l);
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
                          void* v_dst, const Launch& l);
+// n 32-bit words at p set to zero by a kernel (capturable in a graph, unlike
+// a memset node)
+hipError_t launch_fill_zero(uint32_t* p, size_t n, const Launch& l);
 // n_tiles FP8 MFMAs (16 x 16 x 128, E4M3 operands) as the FP8-MFMA attention
 // mode runs them: d = a . b + c per tile (c may be null: zero)
 hipError_t launch_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d, int n_tiles,

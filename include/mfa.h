@@ -188,6 +188,26 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
 int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out,
                int32_t batch, void* hip_stream);
 
+/* mfa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * handle; cfg (host pointer) is checked as by mfa_create and copied, and the
+ * workspace is a static device array of the library (64 MiB on every GPU the
+ * library runs on, held until the process ends). The result is the one
+ * mfa_decode gives on a handle created with the same cfg (same kernels and
+ * split). The call allocates nothing, host or device. Limits: max_batch <=
+ * 65536, and the call's split must fit 2000 partial slots: query rows times
+ * chunks per sequence for a chunked split (mfa_split_tokens gives the chunk;
+ * for example 128 sequences of 4096 tokens in two chunks use 256), or rows
+ * times (ceil(max_context / 256) + 1) for a balanced one; beyond them the
+ * call returns MFA_ERR_UNSUPPORTED before enqueueing anything. Every call on
+ * one GPU shares that workspace: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * The first call on a device enqueues one small clearing kernel on
+ * hip_stream before the attention. Other arguments, ownership and errors as
+ * for mfa_decode. */
+int mfa_decode_noalloc(const mfa_config* cfg, const void* q, const mfa_kv* kv, void* out,
+                       float* lse_out, int32_t batch, void* hip_stream);
+
 /* Multi-token decode (several new tokens per sequence in one step, as
  * multi-token prediction does; Step-3 Key points name it among the future
  * directions): num_tokens query tokens per sequence attend to the same cache.
