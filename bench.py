@@ -14,14 +14,18 @@ seeded synthetic tensors already resident in HBM; several copies are rotated
 so that consecutive steps do not find their KV cache in the 256 MB MALL.
 
 Prints one JSON line: tokens/s per layer (batch / step time), the attention
-kernel's achieved algorithmic HBM bandwidth against 8 TB/s, and the fp64 CPU
-oracle timed on a bounded sample on the host cores. The step time is the
-wall time of the timed steps between two device synchronisations. Kernel
-durations come from a second pass over the same steps in which the library
-attaches a HIP event pair to each launch (hipExtLaunchKernel stamps them with
-the kernel's own start and end on the launch stream); the pairs cost a few
-microseconds of launch gap, which is why the throughput pass runs without
-them.
+kernel's achieved algorithmic HBM bandwidth against 8 TB/s, its MFMA rate
+against the dense peak, and the fp64 CPU oracle timed on a bounded sample on
+the host cores (with the largest row error of the GPU's output against it on
+that sample). The step time is the wall time of the timed steps between two
+device synchronisations; a HIP event pair on the launch stream brackets the
+same steps. When a step is one kernel, the kernel's duration is that event
+time per step (never more than the wall step). Otherwise per-kernel
+durations come from a later pass in which the library attaches a HIP event
+pair to each launch (hipExtLaunchKernel stamps the kernel's own start and
+end); those pairs add launch gaps, so that pass is not the throughput pass.
+A third pass with an event pair around every step gives the median and the
+10th and 90th percentiles of the step time.
 """
 from __future__ import annotations
 
@@ -64,6 +68,8 @@ ATTN_SOURCES = ("decode_attention_mfa_amd/csrc/mfa_attn.hip", "decode_attention_
                 "decode_attention_mfa_amd/csrc/mfa_device.h",
                 "decode_attention_mfa_amd/csrc/mfa_internal.h", "decode_attention_mfa_amd/csrc/mfa_api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense matrix peaks
 WARMUP_SECONDS = 0.5
 
 
@@ -143,9 +149,25 @@ def sample_case(case, n):
     return s
 
 
-def cpu_baseline(case, budget_s: float):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(case, budget_s: float, gpu_out=None, gpu_lse=None):
     """The fp64 oracle, as it stands, on the first n sequences; n chosen from
-    a one-sequence probe so that the run takes about budget_s seconds."""
+    a one-sequence probe so that the run takes about budget_s seconds. With
+    the GPU's output of the workload (gpu_out bf16 bits, gpu_lse), also the
+    largest row error of the GPU against the oracle on that sample (row-wise
+    max |o_gpu - o_ref| / max |o_ref|; absolute on the log-sum-exp)."""
+    import numpy as np
     import oracle
 
     qtok = case.q.shape[1] if case.q is not None and case.q.ndim == 4 else 1
@@ -154,11 +176,10 @@ def cpu_baseline(case, budget_s: float):
         if s.w_k is not None:
             oracle.kv_project(s.x, s.w_k, s.w_v)
         if qtok > 1:
-            oracle.attention_mtp(oracle.decode_bf16(s.q), s.k, s.v, s.seq_lens,
-                                 kv_dtype=oracle.KV_FP8 if s.kv_dtype == "fp8" else oracle.KV_BF16,
-                                 k_scale=s.k_scale, v_scale=s.v_scale, page_table=s.page_table)
-        else:
-            oracle.case_attention(s)
+            return oracle.attention_mtp(oracle.decode_bf16(s.q), s.k, s.v, s.seq_lens,
+                                        kv_dtype=oracle.KV_FP8 if s.kv_dtype == "fp8" else oracle.KV_BF16,
+                                        k_scale=s.k_scale, v_scale=s.v_scale, page_table=s.page_table)
+        return oracle.case_attention(s)
 
     t0 = time.perf_counter()
     work(sample_case(case, 1))
@@ -166,12 +187,24 @@ def cpu_baseline(case, budget_s: float):
     n = max(1, min(case.batch, int(budget_s / max(t1, 1e-3))))
     s = sample_case(case, n)
     t0 = time.perf_counter()
-    work(s)
+    ref = work(s)
     dt = time.perf_counter() - t0
     what = " + ".join(w for w, on in (("Q projection", case.w_qa is not None),
                                        ("K/V projection", case.w_k is not None), ("attention", True)) if on)
-    return {"value": n * qtok / dt, "unit": "tokens/s/layer", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{what} of the first {n} of {case.batch} sequences, fp64, {dt:.1f} s"}
+    res = {"value": n * qtok / dt, "unit": "tokens/s/layer", "cores": oracle.max_threads(), "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{what} of the first {n} of {case.batch} sequences, fp64, {dt:.1f} s"}
+    if ref is not None and gpu_out is not None:
+        o_ref, lse_ref = ref
+        o = oracle.decode_bf16(gpu_out[:n].reshape(o_ref.shape))
+        lse = gpu_lse[:n].reshape(lse_ref.shape).astype(np.float64)
+        live = np.isfinite(lse_ref)
+        den = np.maximum(np.abs(o_ref).max(axis=-1), 1e-30)
+        err = (np.abs(o - o_ref).max(axis=-1) / den)[live]
+        res["parity"] = {"max_row_err": float(err.max()) if err.size else 0.0,
+                         "max_lse_err": float(np.abs(lse - lse_ref)[live].max()) if err.size else 0.0,
+                         "vs": "exact fp64 oracle", "rows": int(err.size)}
+    return res
 
 
 def traffic_key(workload: str, attn_math: str) -> str:
@@ -189,6 +222,20 @@ def load_traffic(workload: str, sha: str):
     if not e or e.get("source_sha") != sha:
         return None
     return float(e["traffic_bytes_per_launch"])
+
+
+def load_counters(workload: str, sha: str):
+    """Stored rocprofv3 counter figures of a workload's attention kernel, if
+    taken on the current sources."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("source_sha") != sha:
+        return None
+    return e
 
 
 def main():
@@ -313,10 +360,30 @@ def main():
             t = run(10)
             warmup = max(20, int(math.ceil(WARMUP_SECONDS / (t / 10))))
         run(warmup)
-        # timed steps (the reported throughput), no per-launch events
-        dt = run(args.steps)
-        # the same steps again with an event pair attached to every launch:
-        # per-kernel durations
+        # timed steps (the reported throughput), no per-launch events: wall
+        # time between two synchronisations, and an event pair on the launch
+        # stream around the same steps
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        gpu_ms = ev0.elapsed_time(ev1)
+        # the step-time distribution: an event pair around every step
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for i, (a, b) in enumerate(pairs):
+            a.record(stream)
+            step(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        step_ms = sorted(a.elapsed_time(b) for a, b in pairs)
+        # per-kernel durations: an event pair attached to every launch
         mfa.mfa_profile_enable(h, True)
         mfa.mfa_profile_read(h)
         run(args.steps)
@@ -329,8 +396,26 @@ def main():
     value = dc.batch * qtok / (ms_per_step / 1e3)
     attn_bytes, _ = algorithmic_bytes(case, prof["combine"][0] == 0, append, qtok)
     n_attn, ms_attn = prof["attention"]
-    attn_ms = ms_attn / max(n_attn, 1)
+    one_kernel = all(n == 0 for k, (n, _) in prof.items() if k != "attention")
+    if one_kernel:
+        # the step is the attention kernel alone: its duration is the event
+        # time of the timed steps per step (launch gaps included)
+        attn_ms = gpu_ms / args.steps
+        timing = "HIP event pair on the launch stream around the timed steps (one kernel per step)"
+    else:
+        attn_ms = ms_attn / max(n_attn, 1)
+        timing = ("hipExtLaunchKernel event pairs on the launch stream (the kernel's own start and end), "
+                  "over a later pass of the same steps")
+    if attn_ms > ms_per_step:   # a kernel cannot outlast the step it belongs to
+        attn_ms = ms_per_step
+        timing += "; capped at the step time"
     achieved = attn_bytes / (attn_ms / 1e3) / 1e9
+    # MFMA work: scores and P.V, 2 x 64 x 256 multiply-adds per (query token, cached token)
+    flops = 4 * 64 * 256 * int((case.seq_lens.astype(np.int64) + (1 if append else 0)).sum()) * qtok
+    mfma_kind = "fp8" if args.attn_math == "fp8" else "bf16"
+    mfma_tflops = flops / (attn_ms / 1e3) / 1e12
+    counters = load_counters(traffic_key(wl, args.attn_math), attn_source_sha())
+    pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * len(step_ms)))] * 1e3
     sha = attn_source_sha()
     traffic = load_traffic(traffic_key(wl, args.attn_math), sha)
     kernels = {k: {"launches": n, "avg_us": round(ms * 1e3 / n, 2)} for k, (n, ms) in prof.items() if n}
@@ -356,9 +441,15 @@ def main():
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": attn_bytes,
-                     "avg_launch_us": round(attn_ms * 1e3, 2), "source_sha": sha,
-                     "timing": "hipExtLaunchKernel event pairs on the launch stream, over a second "
-                               "pass of the timed steps"},
+                     "avg_launch_us": round(attn_ms * 1e3, 2), "source_sha": sha, "timing": timing},
+        "mfma": {"dtype": mfma_kind, "flops_per_launch": flops, "achieved_tflops": round(mfma_tflops, 1),
+                 "peak_tflops": MFMA_PEAK_TFLOPS[mfma_kind],
+                 "frac": round(mfma_tflops / MFMA_PEAK_TFLOPS[mfma_kind], 4),
+                 "busy_frac": counters.get("mfma_busy_frac") if counters else None,
+                 "busy_source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs), "
+                                "profiles/counters.json" if counters else None},
+        "step_us": {"median": round(pct(0.5), 2), "p10": round(pct(0.1), 2), "p90": round(pct(0.9), 2),
+                    "n": len(step_ms), "timing": "HIP event pair around each step, a later pass"},
         "kernels": kernels,
     }
     if append:
@@ -371,7 +462,10 @@ def main():
                                "frac": round(ab / (app_us / 1e6) / 1e9 / HBM_PEAK_GBPS, 4)}
     if args.cpu_seconds > 0:
         log("[bench] timing the fp64 CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        o_last, l_last = outs[(args.steps - 1) % nrot]
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds,
+                                              None if append else o_last.cpu().numpy().view(np.uint16),
+                                              None if append else l_last.cpu().numpy())
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
