@@ -9,6 +9,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <unordered_set>
 #include <vector>
 
 #include "mfa.h"
@@ -30,8 +31,6 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(MFA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr uint32_t kMagic = 0x4d464131u;   // "MFA1"
-constexpr uint32_t kDead = 0xdeadbeefu;
 constexpr int kMinAutoSplit = 256;
 constexpr int kMaxAutoSplit = 2048;
 
@@ -74,7 +73,6 @@ struct Profiler {
 };
 
 struct mfa_ctx {
-    uint32_t magic;
     Profiler prof;
     mfa_config cfg;
     int device;
@@ -91,7 +89,18 @@ struct mfa_ctx {
     float* kv_part;        // [2][hidden / kKvRowsPerSplit][max_batch][256]
 };
 
-static bool valid_handle(mfa_handle h) { return h != nullptr && h->magic == kMagic; }
+// Live handles, so that a pointer that is not one (never created, or
+// destroyed) is rejected without reading the memory it points at.
+static std::mutex g_handles_mutex;
+static std::unordered_set<const mfa_ctx*>& live_handles() {
+    static std::unordered_set<const mfa_ctx*>* set = new std::unordered_set<const mfa_ctx*>();
+    return *set;
+}
+static bool valid_handle(mfa_handle h) {
+    if (!h) return false;
+    std::lock_guard<std::mutex> lock(g_handles_mutex);
+    return live_handles().count(h) != 0;
+}
 
 // Launch `fn(launch)` on `st`; when profiling is on, with the next event pair
 // of the ring attached to the kernel's own start and end.
@@ -265,6 +274,11 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     // one more slot per sequence than chunks: a balanced split may cut a
     // sequence into ceil(steps / 4) + 1 pieces
     const int64_t nparts = (int64_t)c.max_batch * (max_chunks + 1);
+    // bounds that keep every size below in int64 (and far beyond any GPU's memory)
+    if (max_chunks > (1 << 24) || nparts > (int64_t)1 << 31)
+        return fail(MFA_ERR_INVALID, "mfa_create: max_batch * max_context too large");
+    if ((int64_t)c.max_batch * c.hidden > (int64_t)1 << 40)
+        return fail(MFA_ERR_INVALID, "mfa_create: max_batch * hidden too large");
     const int64_t bytes_o = nparts * mfa::kHeads * mfa::kHeadDim * 2;   // bf16 partials
     const int64_t bytes_lse = nparts * mfa::kHeads * 4;
     const int64_t bytes_c = (int64_t)(c.hidden / mfa::kQprojRowsPerSplit) * c.max_batch * c.q_rank * 4;
@@ -272,8 +286,6 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
     const int64_t bytes_kv = 2 * (int64_t)(c.hidden / mfa::kKvRowsPerSplit) * c.max_batch * mfa::kHeadDim * 4;
     const int64_t bytes_sumsq = (int64_t)(c.q_rank / 64) * c.max_batch * 4;
     const int64_t bytes_qctr = (int64_t)((c.max_batch + 31) / 32) * (c.q_rank / 64) * 4;
-    if (max_chunks > (1 << 24) || nparts > (int64_t)1 << 31)
-        return fail(MFA_ERR_INVALID, "mfa_create: max_batch * max_context too large");
 
     mfa_ctx* h = new (std::nothrow) mfa_ctx();
     if (!h) return fail(MFA_ERR_NOMEM, "mfa_create: host allocation failed");
@@ -317,7 +329,10 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
         delete h;
         return hip_fail(e, "mfa_create: clearing the workspace");
     }
-    h->magic = kMagic;
+    {
+        std::lock_guard<std::mutex> lock(g_handles_mutex);
+        live_handles().insert(h);
+    }
     *out = h;
     return MFA_OK;
 }
@@ -325,8 +340,10 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
 int mfa_destroy(mfa_handle h) {
     g_last_error[0] = 0;
     if (!h) return MFA_OK;
-    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_destroy: not a live handle");
-    h->magic = kDead;
+    {
+        std::lock_guard<std::mutex> lock(g_handles_mutex);
+        if (live_handles().erase(h) == 0) return fail(MFA_ERR_INVALID, "mfa_destroy: not a live handle");
+    }
     profiler_release(h->prof);
     (void)hipFree(h->part_o);
     (void)hipFree(h->part_lse);
@@ -439,7 +456,6 @@ static mfa::KvView make_view(const mfa_ctx* h, const mfa_kv* kv, int32_t max_len
 // mfa_decode (qtok 1) and mfa_decode_mtp (qtok query tokens per sequence).
 static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok, void* out, float* lse_out,
                        int32_t batch, void* hip_stream, const char* fn) {
-    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "%s: not a live handle", fn);
     if (!q || !out) return fail(MFA_ERR_INVALID, "%s: null q or out", fn);
     if (qtok < 1 || qtok > mfa::kMaxQueryTokens)
         return fail(MFA_ERR_INVALID, "%s: num_tokens %d outside [1, %d]", fn, qtok, mfa::kMaxQueryTokens);
@@ -516,12 +532,14 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
 int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out, int32_t batch,
                void* hip_stream) {
     g_last_error[0] = 0;
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_decode: not a live handle");
     return decode_impl(h, q, kv, 1, out, lse_out, batch, hip_stream, "mfa_decode");
 }
 
 int mfa_decode_mtp(mfa_handle h, const void* q, const mfa_kv* kv, int32_t num_tokens, void* out, float* lse_out,
                    int32_t batch, void* hip_stream) {
     g_last_error[0] = 0;
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_decode_mtp: not a live handle");
     return decode_impl(h, q, kv, num_tokens, out, lse_out, batch, hip_stream, "mfa_decode_mtp");
 }
 
@@ -576,7 +594,6 @@ int mfa_decode_noalloc(const mfa_config* cfg, const void* q, const mfa_kv* kv, v
     // kNoAllocSlots partial row blocks, then their log-sum-exps); the call's
     // split is checked against kNoAllocSlots in decode_impl
     mfa_ctx h{};
-    h.magic = kMagic;
     h.cfg = c;
     h.num_cu = sl.num_cu;
     (void)hipGetDevice(&h.device);
@@ -586,7 +603,6 @@ int mfa_decode_noalloc(const mfa_config* cfg, const void* q, const mfa_kv* kv, v
     h.part_o = (float*)(sl.ptr + kNoAllocCounterBytes);
     h.part_lse = (float*)(sl.ptr + kNoAllocCounterBytes + kNoAllocSlots * mfa::kHeads * mfa::kHeadDim * 2);
     rc = decode_impl(&h, q, kv, 1, out, lse_out, batch, hip_stream, "mfa_decode_noalloc");
-    h.magic = kDead;
     return rc;
 }
 

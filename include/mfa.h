@@ -23,6 +23,11 @@
  *   - Arguments are checked on the host before any launch; on error the call
  *     enqueues nothing, returns a negative MFA_ERR_* status and records a
  *     message readable with mfa_last_error() (thread-local).
+ *   - A handle argument must be a live handle (created by mfa_create, not yet
+ *     destroyed): the library keeps a registry of live handles, so a NULL,
+ *     destroyed or foreign pointer is rejected with MFA_ERR_INVALID without
+ *     the memory it points at being read. Destroying a handle while another
+ *     thread is inside a call on it is the caller's race.
  *   - A device fault (for example a page index outside the pool) is not
  *     detected; it surfaces at the caller's next synchronisation.
  *   - A handle may be used by one stream at a time: calls that overlap on
@@ -300,8 +305,10 @@ int mfa_profile_enable(mfa_handle h, int enable);
  * between reads (older ones are overwritten). */
 int mfa_profile_read(mfa_handle h, int32_t* launches, double* total_ms);
 
-/* Release the handle and its workspace. NULL is accepted. The caller must
- * ensure no enqueued call that uses the handle is still running. */
+/* Release the handle and its workspace. NULL is accepted (MFA_OK); a pointer
+ * that is not a live handle (already destroyed, never created) returns
+ * MFA_ERR_INVALID and frees nothing. The caller must ensure no enqueued call
+ * that uses the handle is still running. */
 int mfa_destroy(mfa_handle h);
 
 /* Static text for a status code. */
