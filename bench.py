@@ -43,10 +43,12 @@ sys.path.insert(0, ROOT)
 METRIC = "MFA decode tokens/s per layer (1 GPU) + achieved HBM GB/s vs roofline"
 HBM_PEAK_GBPS = 8000.0
 WORKLOADS = {"tiny": 1, "full_layer": 2, "fp8_contig": 3, "paged_ragged": 4, "long_splitk": 5,
-             "decode_step": 2, "paged_append": 4, "fp8_mtp2": 3, "fp8_mtp4": 3, "fp8_gqa2": 3, "fp8_gqa4": 3}
+             "decode_step": 2, "paged_append": 4, "fp8_mtp2": 3, "fp8_mtp4": 3, "fp8_gqa2": 3, "fp8_gqa4": 3,
+             "bf16_contig": 3, "bf16_gqa2": 3, "bf16_gqa4": 3}
 APPEND = ("decode_step", "paged_append")
 MTP = {"fp8_mtp2": 2, "fp8_mtp4": 4}   # query tokens per sequence
 GQA = {"fp8_gqa2": 2, "fp8_gqa4": 4}   # K/V heads (head-sharing comparison)
+GQA_BF16 = {"bf16_contig": 1, "bf16_gqa2": 2, "bf16_gqa4": 4}   # the same with a bf16 cache
 DESCRIPTION = {
     "tiny": "B=1, L=256, bf16 KV, contiguous, decode only",
     "full_layer": "B=32, L=4096, bf16 KV, contiguous, Q projection 7168->2048 (RMSNorm)->64x256 + decode",
@@ -61,6 +63,9 @@ DESCRIPTION = {
     "fp8_mtp4": "B=128, L=4096, FP8-E4M3 KV, contiguous, 4 query tokens per sequence (multi-token decode)",
     "fp8_gqa2": "B=128, L=4096, FP8-E4M3 KV, contiguous, 64 query heads on 2 K/V heads (grouped-query comparison)",
     "fp8_gqa4": "B=128, L=4096, FP8-E4M3 KV, contiguous, 64 query heads on 4 K/V heads (grouped-query comparison)",
+    "bf16_contig": "B=128, L=4096, bf16 KV, contiguous, 64 query heads on 1 K/V head (MFA, BF16-attention setting)",
+    "bf16_gqa2": "B=128, L=4096, bf16 KV, contiguous, 64 query heads on 2 K/V heads (grouped-query comparison)",
+    "bf16_gqa4": "B=128, L=4096, bf16 KV, contiguous, 64 query heads on 4 K/V heads (grouped-query comparison)",
 }
 # sources that decide the attention kernel's memory traffic (kernel, launch
 # shape, split and merge policy); the stored HBM counters hold for this hash
@@ -281,7 +286,12 @@ def main():
     t0 = time.perf_counter()
     append = wl in APPEND
     qtok = MTP.get(wl, 1)
-    case = synth.gqa_case(GQA[wl]) if wl in GQA else synth.config_case(WORKLOADS[wl], append=append)
+    if wl in GQA:
+        case = synth.gqa_case(GQA[wl])
+    elif wl in GQA_BF16:
+        case = synth.gqa_case(GQA_BF16[wl], kv_dtype="bf16")
+    else:
+        case = synth.config_case(WORKLOADS[wl], append=append)
     if qtok > 1:
         case.q = synth.mtp_queries(case.batch, qtok, case.seed)
     log(f"[bench] generated in {time.perf_counter() - t0:.1f} s")

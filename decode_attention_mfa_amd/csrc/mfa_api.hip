@@ -167,14 +167,23 @@ static int32_t choose_split(const mfa_ctx* h, int32_t batch, int32_t max_len, in
     return (int32_t)c;
 }
 
-// The chunked split of a call with `rows` query-row sets: the chunk and the
-// number of head groups per (row set, chunk). In the FP8-MFMA mode the 64
-// heads may go to two workgroups of 32 when the doubled grid still fits on
-// the compute units at once: both read the same K/V rows (the second from
-// L2), and a sequence then needs half as many chunks, so fewer partials to
-// merge. With bf16 MFMAs each workgroup would widen every FP8 row itself,
-// and that doubled VALU work costs more than the merges it saves.
-static void plan_chunks(const mfa_ctx* h, int32_t rows, int32_t max_len, int32_t* chunk, int32_t* nh) {
+// The chunked split of a call with `rows` query-row sets (qtok query tokens
+// per sequence): the chunk and the number of head groups per (row set,
+// chunk). Head groups read the same K/V rows (the later ones mostly from
+// the XCD's L2, their block indices 8 apart).
+//   - bf16 caches, one query token, a grid that would use at most a quarter
+//     of the compute units: four groups of 16 heads on the same chunks
+//     (each group's piece then has a quarter of the MFMA and softmax work;
+//     the result is bitwise the one of 64-head workgroups). With more
+//     workgroups the groups' repeated K/V reads cost more than they save:
+//     the bf16 step loop waits on its loads (two 64 KB steps in the ring);
+//   - the FP8-MFMA mode: two groups of 32 on chunks twice as long when the
+//     doubled grid fits, so a sequence needs half as many chunks;
+//   - FP8 caches with bf16 MFMAs keep 64 heads per workgroup: each group
+//     would widen every FP8 row itself, and that VALU work costs more than
+//     the merges it saves.
+static void plan_chunks(const mfa_ctx* h, int32_t rows, int32_t qtok, int32_t max_len, int32_t* chunk,
+                        int32_t* nh) {
     if (h->cfg.kv_heads > 1) {   // grouped caches: one workgroup per (row set, chunk, K/V head)
         *nh = h->cfg.kv_heads;
         *chunk = choose_split(h, *nh * rows, max_len, mfa::kMaxPagedChunkSteps * mfa::kStep);
@@ -182,6 +191,11 @@ static void plan_chunks(const mfa_ctx* h, int32_t rows, int32_t max_len, int32_t
     }
     *nh = 1;
     *chunk = choose_split(h, rows, max_len);
+    if (h->cfg.kv_dtype == MFA_DTYPE_BF16 && qtok == 1 && max_len > 0) {
+        const int64_t n = (max_len + *chunk - 1) / *chunk;
+        if (4 * (int64_t)rows * n <= h->num_cu) *nh = 4;
+        return;
+    }
     if (h->cfg.attn_math != MFA_ATTN_FP8_MFMA || max_len <= 0) return;
     // chunks up to the paged limit: with two workgroups per chunk, the
     // longer chunk still leaves every compute unit one workgroup
@@ -245,10 +259,8 @@ static int validate_config(const mfa_config* cfg, mfa_config* out, const char* f
     if (c.kv_heads == 0) c.kv_heads = 1;
     if (c.kv_heads != 1 && c.kv_heads != 2 && c.kv_heads != 4)
         return fail(MFA_ERR_INVALID, "%s: kv_heads must be 1, 2 or 4 (got %d)", fn, c.kv_heads);
-    if (c.kv_heads > 1 && (c.kv_dtype != MFA_DTYPE_FP8_E4M3 || c.attn_math != MFA_ATTN_BF16_MFMA ||
-                           c.split_tokens == MFA_SPLIT_BALANCED))
-        return fail(MFA_ERR_UNSUPPORTED,
-                    "%s: kv_heads > 1 needs an FP8 cache, MFA_ATTN_BF16_MFMA and chunked splits", fn);
+    if (c.kv_heads > 1 && (c.attn_math != MFA_ATTN_BF16_MFMA || c.split_tokens == MFA_SPLIT_BALANCED))
+        return fail(MFA_ERR_UNSUPPORTED, "%s: kv_heads > 1 needs MFA_ATTN_BF16_MFMA and chunked splits", fn);
 
     *out = c;
     return MFA_OK;
@@ -362,7 +374,7 @@ int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32
     if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;
     if (use_balanced(h, batch, max_seq_len, min_seq_len)) return 0;
     int32_t chunk, nh;
-    plan_chunks(h, batch, max_seq_len, &chunk, &nh);
+    plan_chunks(h, batch, 1, max_seq_len, &chunk, &nh);
     return chunk;
 }
 
@@ -371,7 +383,7 @@ int32_t mfa_head_groups(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_
     if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;
     if (use_balanced(h, batch, max_seq_len, min_seq_len)) return 1;
     int32_t chunk, nh;
-    plan_chunks(h, batch, max_seq_len, &chunk, &nh);
+    plan_chunks(h, batch, 1, max_seq_len, &chunk, &nh);
     return nh;
 }
 
@@ -500,7 +512,7 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
         workgroups = (int)g;
     } else {
         a.balanced = 0;
-        plan_chunks(h, rows, max_len, &a.chunk, &a.nh);
+        plan_chunks(h, rows, qtok, max_len, &a.chunk, &a.nh);
         a.kv_groups = h->cfg.kv_heads;
         a.n_chunk = (max_len + a.chunk - 1) / a.chunk;
         if (a.n_chunk < 1) a.n_chunk = 1;

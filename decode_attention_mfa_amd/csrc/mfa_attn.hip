@@ -570,6 +570,12 @@ hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgr
         if (a.qtok > 1)
             return paged ? launch_kernel(mfa_attn_ws_split_kernel<false, true, true, false, 4>, grid, block, l, a)
                          : launch_kernel(mfa_attn_ws_split_kernel<false, false, true, false, 4>, grid, block, l, a);
+        if (a.nh == 4)   // four head groups of 16 (or four K/V heads)
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<false, true, false, false, 1>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, false, 1>, grid, block, l, a);
+        if (a.nh == 2)
+            return paged ? launch_kernel(mfa_attn_ws_split_kernel<false, true, false, false, 2>, grid, block, l, a)
+                         : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, false, 2>, grid, block, l, a);
         return paged ? launch_kernel(mfa_attn_ws_split_kernel<false, true, false, false, 4>, grid, block, l, a)
                      : launch_kernel(mfa_attn_ws_split_kernel<false, false, false, false, 4>, grid, block, l, a);
     }

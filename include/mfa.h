@@ -105,9 +105,9 @@ typedef struct {
                               Transformer Models from Multi-Head Checkpoints", named on the
                               DeepSeek-V4 references), for comparing head-sharing schemes:
                               query head h reads K/V head h / (64 / G), the cache holds G
-                              heads per token (layouts in mfa_kv). G > 1 needs an FP8 cache
-                              and MFA_ATTN_BF16_MFMA; mfa_decode only (not mfa_decode_mtp,
-                              mfa_kv_append or mfa_debug_gather_kv) and not
+                              heads per token (layouts in mfa_kv). G > 1 needs
+                              MFA_ATTN_BF16_MFMA (bf16 or FP8 cache); mfa_decode only (not
+                              mfa_decode_mtp, mfa_kv_append or mfa_debug_gather_kv) and not
                               MFA_SPLIT_BALANCED (else MFA_ERR_UNSUPPORTED) */
 } mfa_config;
 
@@ -258,9 +258,11 @@ int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32
 /* The number of workgroups that share the 64 query heads of one (sequence,
  * chunk) in that split: 1; 2 (heads 0-31 and 32-63, which then read the same
  * K/V rows, the second read from L2) with attn_math MFA_ATTN_FP8_MFMA and a
- * chunked split whose doubled grid fits on the compute units at once; or
- * kv_heads for a grouped-query cache (one workgroup per K/V head). The
- * result of mfa_decode does not depend on it. Negative status on error. */
+ * chunked split whose doubled grid fits on the compute units at once; 4
+ * (16 heads each) for a bf16 cache whose grid would otherwise use at most a
+ * quarter of the compute units; or kv_heads for a grouped-query cache (one
+ * workgroup per K/V head). For a given chunk the result of mfa_decode does
+ * not depend on it. Negative status on error. */
 int32_t mfa_head_groups(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len);
 
 /* Test support: copy the logical K and V rows t < L_b of sequence b into

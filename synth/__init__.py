@@ -243,12 +243,17 @@ def config_case(i: int, *, batch: Optional[int] = None, scale_len: float = 1.0,
 
 
 def gqa_case(kv_heads: int, *, batch: Optional[int] = None, scale_len: float = 1.0,
-             paged: bool = False) -> Case:
+             paged: bool = False, kv_dtype: str = "fp8") -> Case:
     """The FP8 workload's recipe (B = 128, L = 4096, N(0,1) Q and K/V, E4M3
     codes with per-tensor amax scales) with ``kv_heads`` K/V heads per token,
     for comparing head-sharing schemes at equal query shape. Seed 1003 for
-    one head (the FP8 workload itself), 1100 + G otherwise."""
+    one head (the FP8 workload itself), 1100 + G otherwise. kv_dtype "bf16":
+    the same shapes with a bf16 cache (seed 1200 + G), the BF16-attention
+    setting of the comparison."""
     B = batch or 128
+    if kv_dtype == "bf16":
+        return make_case(f"bf16_gqa{kv_heads}", B, max(1, int(4096 * scale_len)), "bf16", seed=1200 + kv_heads,
+                         paged=paged, kv_heads=kv_heads)
     seed = 1003 if kv_heads == 1 else 1100 + kv_heads
     return make_case(f"fp8_gqa{kv_heads}", B, max(1, int(4096 * scale_len)), "fp8", seed=seed,
                      paged=paged, kv_heads=kv_heads)

@@ -107,7 +107,7 @@ static void bad_configs() {
         {[](mfa_config& c) { c.attn_math = 5; }, MFA_ERR_INVALID},
         {[](mfa_config& c) { c.kv_dtype = MFA_DTYPE_BF16; c.attn_math = MFA_ATTN_FP8_MFMA; }, MFA_ERR_UNSUPPORTED},
         {[](mfa_config& c) { c.kv_heads = 3; }, MFA_ERR_INVALID},
-        {[](mfa_config& c) { c.kv_heads = 2; c.kv_dtype = MFA_DTYPE_BF16; }, MFA_ERR_UNSUPPORTED},
+        {[](mfa_config& c) { c.kv_heads = 2; c.attn_math = MFA_ATTN_FP8_MFMA; }, MFA_ERR_UNSUPPORTED},
         {[](mfa_config& c) { c.kv_heads = 4; c.split_tokens = MFA_SPLIT_BALANCED; }, MFA_ERR_UNSUPPORTED},
         {[](mfa_config& c) { c.max_batch = 1 << 30; c.max_context = 1 << 30; }, MFA_ERR_INVALID},
     };
@@ -331,12 +331,12 @@ int main(int argc, char** argv) {
                         c.attn_math = MFA_ATTN_FP8_MFMA;
                         sweep(c);
                         c.attn_math = MFA_ATTN_BF16_MFMA;
-                        if (split != MFA_SPLIT_BALANCED)
-                            for (int g : {2, 4}) {
-                                c.kv_heads = g;
-                                sweep(c);
-                            }
                     }
+                    if (split != MFA_SPLIT_BALANCED)
+                        for (int g : {2, 4}) {
+                            c.kv_heads = g;
+                            sweep(c);
+                        }
                 }
         for (int cu : {1, 8, 80, 304}) {   // planning for other compute-unit counts
             stub_set_num_cu(cu);

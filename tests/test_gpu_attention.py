@@ -76,6 +76,44 @@ def test_ragged_tails(kv):
     check_parity(case, split_tokens=0, label=f"ragged tails {kv} auto split")
 
 
+@pytest.mark.parametrize("lens", [[256], [1, 700], [4096, 3000, 65]])
+def test_bf16_head_groups(lens):
+    """bf16 caches whose grid would use at most a quarter of the compute units
+    run four workgroups of 16 heads per (sequence, chunk): parity with the
+    oracle, and the output is bitwise the one of 64-head workgroups on the
+    same chunks (the head groups change no arithmetic of a head), here from a
+    batch repeated until its grid is large enough for 64-head workgroups."""
+    m, hz = _mfa()
+    case = synth.make_case("bf16_hg", len(lens), lens, "bf16", seed=81, kv_slack=3)
+    dc = hz.to_device(case)
+    h = hz.create_handle(dc, split_tokens=0)
+    try:
+        groups = m.mfa_head_groups(h, dc.batch, dc.max_len, dc.min_len)
+        chunk = m.mfa_split_tokens(h, dc.batch, dc.max_len, dc.min_len)
+    finally:
+        m.mfa_destroy(h)
+    _say(f"[bf16 head groups] lens={lens}: {groups} groups, chunk {chunk}")
+    assert groups == 4
+    out, _ = check_parity(case, split_tokens=0, label="bf16 head groups")
+    reps = 1
+    while True:
+        reps *= 2
+        big = synth.Case(name="rep", batch=case.batch * reps, kv_dtype="bf16", seq_lens=np.tile(case.seq_lens, reps),
+                         k=np.tile(case.k, (reps, 1, 1)), v=np.tile(case.v, (reps, 1, 1)),
+                         q=np.tile(case.q, (reps, 1, 1)), k_scale=case.k_scale, v_scale=case.v_scale)
+        bdc = hz.to_device(big)
+        h = hz.create_handle(bdc, split_tokens=chunk)
+        try:
+            g1 = m.mfa_head_groups(h, bdc.batch, bdc.max_len, bdc.min_len)
+        finally:
+            m.mfa_destroy(h)
+        if g1 == 1:
+            break
+        assert reps < 4096
+    out1, _, _ = hz.run_case(bdc, split_tokens=chunk)
+    assert torch.equal(out.cpu(), out1.cpu()[:case.batch])
+
+
 def test_empty_sequences():
     case = synth.make_case("empty", 4, [0, 5, 0, 300], "fp8", seed=78)
     check_parity(case, split_tokens=128, label="empty sequences")

@@ -60,33 +60,40 @@ def _check(case, split, label, sample=None):
         assert np.all(o[~nz] == 0) and np.all(np.isneginf(lse[~nz]))
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
 @pytest.mark.parametrize("G", [2, 4])
 @pytest.mark.parametrize("split", [0, 256, 1024])
-def test_gqa_contiguous(G, split):
+def test_gqa_contiguous(kv, G, split):
     """Ragged tails, an empty sequence, one and two chunks (merged in the
     kernel) and many chunks (combine kernel)."""
     L = [0, 1, 63, 64, 65, 300, 1000, 2049]
-    case = synth.make_case("gqa", len(L), L, "fp8", seed=400 + G, kv_slack=5, kv_heads=G)
-    _check(case, split, "contiguous")
+    case = synth.make_case("gqa", len(L), L, kv, seed=400 + G, kv_slack=5, kv_heads=G)
+    _check(case, split, f"contiguous {kv}")
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
 @pytest.mark.parametrize("G", [2, 4])
-def test_gqa_paged(G):
+def test_gqa_paged(kv, G):
     L = [5, 64, 129, 700, 1500, 0]
-    case = synth.make_case("gqa_paged", len(L), L, "fp8", seed=410 + G, paged=True, kv_heads=G)
-    _check(case, 256, "paged")
-    _check(case, 0, "paged, auto split")
+    case = synth.make_case("gqa_paged", len(L), L, kv, seed=410 + G, paged=True, kv_heads=G)
+    _check(case, 256, f"paged {kv}")
+    _check(case, 0, f"paged {kv}, auto split")
 
 
-def test_gqa_groups_are_independent():
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_gqa_groups_are_independent(kv):
     """Changing K/V head 1's rows changes only its query heads' outputs."""
     m, hz = _mfa()
-    case = synth.make_case("gqa_ind", 2, [300, 77], "fp8", seed=420, kv_heads=2)
     outs = []
     for variant in range(2):
-        c = synth.make_case("gqa_ind", 2, [300, 77], "fp8", seed=420, kv_heads=2)
+        c = synth.make_case("gqa_ind", 2, [300, 77], kv, seed=420, kv_heads=2)
         if variant:
-            c.k[:, 1] = np.random.default_rng(421).integers(0, 0x7e, size=c.k[:, 1].shape, dtype=np.uint8)
+            # other finite values: E4M3 codes below NaN's, or bf16 bits of N(0,1) draws
+            g = np.random.default_rng(421)
+            if kv == "fp8":
+                c.k[:, 1] = g.integers(0, 0x7e, size=c.k[:, 1].shape, dtype=np.uint8)
+            else:
+                c.k[:, 1] = synth.bf16_bits(g.standard_normal(c.k[:, 1].shape).astype(np.float32))
         dc = hz.to_device(c)
         h = hz.create_handle(dc, split_tokens=0)
         try:
@@ -99,12 +106,13 @@ def test_gqa_groups_are_independent():
     assert not torch.equal(outs[0][:, 32:], outs[1][:, 32:])
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
 @pytest.mark.parametrize("G", [2, 4])
-def test_gqa_full_size(G):
+def test_gqa_full_size(kv, G):
     """The comparison workloads at full size (B = 128, L = 4096, G K/V heads)
     in bench.py's configuration: sampled sequences against the oracle."""
-    case = synth.gqa_case(G)
-    _check(case, 0, "full size", sample=np.array([0, 41, 86, 127]))
+    case = synth.gqa_case(G, kv_dtype=kv)
+    _check(case, 0, f"full size {kv}", sample=np.array([0, 41, 86, 127]))
 
 
 def test_gqa_rejected_where_unsupported():
