@@ -44,11 +44,12 @@ METRIC = "MFA decode tokens/s per layer (1 GPU) + achieved HBM GB/s vs roofline"
 HBM_PEAK_GBPS = 8000.0
 WORKLOADS = {"tiny": 1, "full_layer": 2, "fp8_contig": 3, "paged_ragged": 4, "long_splitk": 5,
              "decode_step": 2, "paged_append": 4, "fp8_mtp2": 3, "fp8_mtp4": 3, "fp8_gqa2": 3, "fp8_gqa4": 3,
-             "bf16_contig": 3, "bf16_gqa2": 3, "bf16_gqa4": 3}
+             "bf16_contig": 3, "bf16_gqa2": 3, "bf16_gqa4": 3, "fp8_mla": 3}
 APPEND = ("decode_step", "paged_append")
 MTP = {"fp8_mtp2": 2, "fp8_mtp4": 4}   # query tokens per sequence
 GQA = {"fp8_gqa2": 2, "fp8_gqa4": 4}   # K/V heads (head-sharing comparison)
 GQA_BF16 = {"bf16_contig": 1, "bf16_gqa2": 2, "bf16_gqa4": 4}   # the same with a bf16 cache
+LATENT = ("fp8_mla",)   # latent-cache (MLA-style) comparison
 DESCRIPTION = {
     "tiny": "B=1, L=256, bf16 KV, contiguous, decode only",
     "full_layer": "B=32, L=4096, bf16 KV, contiguous, Q projection 7168->2048 (RMSNorm)->64x256 + decode",
@@ -66,6 +67,8 @@ DESCRIPTION = {
     "bf16_contig": "B=128, L=4096, bf16 KV, contiguous, 64 query heads on 1 K/V head (MFA, BF16-attention setting)",
     "bf16_gqa2": "B=128, L=4096, bf16 KV, contiguous, 64 query heads on 2 K/V heads (grouped-query comparison)",
     "bf16_gqa4": "B=128, L=4096, bf16 KV, contiguous, 64 query heads on 4 K/V heads (grouped-query comparison)",
+    "fp8_mla": "B=128, L=4096, one 512-wide FP8-E4M3 latent row per token as key and value of 64 heads of 512 "
+               "(absorbed MLA-style latent cache, same cache bytes per token as MFA), contiguous",
 }
 # sources that decide the attention kernel's memory traffic (kernel, launch
 # shape, split and merge policy); the stored HBM counters hold for this hash
@@ -78,8 +81,11 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense matrix peaks
 WARMUP_SECONDS = 0.5
 
 
-def attn_kernel_name(split: int, fp8: bool) -> str:
-    """The attention kernel a launch runs: balanced split, or chunks."""
+def attn_kernel_name(split: int, fp8: bool, latent: bool = False) -> str:
+    """The attention kernel a launch runs: balanced split, chunks, or the
+    latent-cache kernel."""
+    if latent:
+        return "mfa_mla_kernel"
     return "mfa_attn_balanced_kernel" if split == 0 else "mfa_attn_ws_split_kernel"
 
 
@@ -109,9 +115,14 @@ def algorithmic_bytes(case, attention_writes_out: bool, append: bool = False, qt
     B = case.batch
     L = case.seq_lens.astype(np.int64) + (1 if append else 0)
     elem = 1 if case.kv_dtype == "fp8" else 2
-    kv = int(L.sum()) * 2 * 256 * elem * getattr(case, "kv_heads", 1)
-    q = B * qtok * 64 * 256 * 2
-    o = B * qtok * 64 * 256 * 2
+    latent = getattr(case, "kv_latent", 0)
+    if latent:   # one latent row per token, read once as key and value; 512-wide Q and output rows
+        kv = int(L.sum()) * latent * elem
+    else:
+        kv = int(L.sum()) * 2 * 256 * elem * getattr(case, "kv_heads", 1)
+    width = latent or 256
+    q = B * qtok * 64 * width * 2
+    o = B * qtok * 64 * width * 2
     meta = B * 4
     if case.paged:
         meta += int(((L + 63) // 64).sum()) * 4
@@ -290,6 +301,8 @@ def main():
         case = synth.gqa_case(GQA[wl])
     elif wl in GQA_BF16:
         case = synth.gqa_case(GQA_BF16[wl], kv_dtype="bf16")
+    elif wl in LATENT:
+        case = synth.latent_case(wl, 128, 4096, seed=1300)
     else:
         case = synth.config_case(WORKLOADS[wl], append=append)
     if qtok > 1:
@@ -421,7 +434,9 @@ def main():
         timing += "; capped at the step time"
     achieved = attn_bytes / (attn_ms / 1e3) / 1e9
     # MFMA work: scores and P.V, 2 x 64 x 256 multiply-adds per (query token, cached token)
-    flops = 4 * 64 * 256 * int((case.seq_lens.astype(np.int64) + (1 if append else 0)).sum()) * qtok
+    # (2 x 64 x 512 with a latent cache)
+    flops = 4 * 64 * (getattr(case, "kv_latent", 0) or 256) * \
+        int((case.seq_lens.astype(np.int64) + (1 if append else 0)).sum()) * qtok
     mfma_kind = "fp8" if args.attn_math == "fp8" else "bf16"
     mfma_tflops = flops / (attn_ms / 1e3) / 1e12
     counters = load_counters(traffic_key(wl, args.attn_math), attn_source_sha())
@@ -447,7 +462,8 @@ def main():
                    "kv_heads": getattr(case, "kv_heads", 1),
                    "input_sets_rotated": nrot, "mall": "cold" if cold else "warm"},
         "step_hbm_gbps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": attn_kernel_name(split, case.kv_dtype == "fp8"),
+        "roofline": {"bound": "hbm", "kernel": attn_kernel_name(split, case.kv_dtype == "fp8",
+                                                                bool(getattr(case, "kv_latent", 0))),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": attn_bytes,

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <string>
@@ -207,6 +208,12 @@ static void plan_chunks(const mfa_ctx* h, int32_t rows, int32_t qtok, int32_t ma
     }
 }
 
+// Latent-cache mode: the chunk for `rows` query rows, two workgroups of 32
+// heads per (row, chunk).
+static int32_t latent_chunk(const mfa_ctx* h, int32_t rows, int32_t max_len) {
+    return choose_split(h, 2 * rows, max_len, mfa::kMaxPagedChunkSteps * mfa::kStep);
+}
+
 extern "C" {
 
 const char* mfa_status_string(int status) {
@@ -261,6 +268,12 @@ static int validate_config(const mfa_config* cfg, mfa_config* out, const char* f
         return fail(MFA_ERR_INVALID, "%s: kv_heads must be 1, 2 or 4 (got %d)", fn, c.kv_heads);
     if (c.kv_heads > 1 && (c.attn_math != MFA_ATTN_BF16_MFMA || c.split_tokens == MFA_SPLIT_BALANCED))
         return fail(MFA_ERR_UNSUPPORTED, "%s: kv_heads > 1 needs MFA_ATTN_BF16_MFMA and chunked splits", fn);
+    if (c.kv_latent != 0 && c.kv_latent != mfa::kLatent)
+        return fail(MFA_ERR_INVALID, "%s: kv_latent must be 0 or %d (got %d)", fn, mfa::kLatent, c.kv_latent);
+    if (c.kv_latent && (c.kv_dtype != MFA_DTYPE_FP8_E4M3 || c.kv_heads > 1 || c.attn_math != MFA_ATTN_BF16_MFMA ||
+                        c.split_tokens == MFA_SPLIT_BALANCED))
+        return fail(MFA_ERR_UNSUPPORTED,
+                    "%s: kv_latent needs an FP8 cache, kv_heads 1, MFA_ATTN_BF16_MFMA and chunked splits", fn);
 
     *out = c;
     return MFA_OK;
@@ -291,7 +304,8 @@ int mfa_create(const mfa_config* cfg, mfa_handle* out) {
         return fail(MFA_ERR_INVALID, "mfa_create: max_batch * max_context too large");
     if ((int64_t)c.max_batch * c.hidden > (int64_t)1 << 40)
         return fail(MFA_ERR_INVALID, "mfa_create: max_batch * hidden too large");
-    const int64_t bytes_o = nparts * mfa::kHeads * mfa::kHeadDim * 2;   // bf16 partials
+    const int64_t row_dim = c.kv_latent ? mfa::kLatent : mfa::kHeadDim;   // output row width
+    const int64_t bytes_o = nparts * mfa::kHeads * row_dim * 2;          // bf16 partials
     const int64_t bytes_lse = nparts * mfa::kHeads * 4;
     const int64_t bytes_c = (int64_t)(c.hidden / mfa::kQprojRowsPerSplit) * c.max_batch * c.q_rank * 4;
     const int64_t bytes_chat = (int64_t)c.max_batch * c.q_rank * 2;
@@ -372,6 +386,7 @@ int mfa_destroy(mfa_handle h) {
 int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len) {
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_split_tokens: not a live handle");
     if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;
+    if (h->cfg.kv_latent) return latent_chunk(h, batch, max_seq_len);
     if (use_balanced(h, batch, max_seq_len, min_seq_len)) return 0;
     int32_t chunk, nh;
     plan_chunks(h, batch, 1, max_seq_len, &chunk, &nh);
@@ -381,6 +396,7 @@ int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32
 int32_t mfa_head_groups(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len) {
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_head_groups: not a live handle");
     if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;
+    if (h->cfg.kv_latent) return 2;
     if (use_balanced(h, batch, max_seq_len, min_seq_len)) return 1;
     int32_t chunk, nh;
     plan_chunks(h, batch, 1, max_seq_len, &chunk, &nh);
@@ -391,6 +407,7 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w, 
               void* q_out, int32_t batch, void* hip_stream) {
     g_last_error[0] = 0;
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_qproj: not a live handle");
+    if (h->cfg.kv_latent) return fail(MFA_ERR_UNSUPPORTED, "mfa_qproj: not for a latent-cache handle");
     if (!x || !w_qa || !rms_w || !w_qb || !q_out)
         return fail(MFA_ERR_INVALID, "mfa_qproj: null tensor pointer");
     if (batch < 1 || batch > h->cfg.max_batch)
@@ -424,7 +441,8 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w, 
 
 static int check_kv(const mfa_ctx* h, const mfa_kv* kv, int32_t batch, const char* fn, int32_t* max_len) {
     if (!kv) return fail(MFA_ERR_INVALID, "%s: null kv", fn);
-    if (!kv->k || !kv->v || !kv->seq_lens) return fail(MFA_ERR_INVALID, "%s: null k, v or seq_lens", fn);
+    if (!kv->k || (!kv->v && !h->cfg.kv_latent) || !kv->seq_lens)
+        return fail(MFA_ERR_INVALID, "%s: null k, v or seq_lens", fn);
     const int32_t ml = kv->max_seq_len > 0 ? kv->max_seq_len : h->cfg.max_context;
     if (kv->max_seq_len < 0 || ml > h->cfg.max_context)
         return fail(MFA_ERR_INVALID, "%s: max_seq_len %d outside [0, max_context %d]", fn, kv->max_seq_len,
@@ -441,7 +459,8 @@ static int check_kv(const mfa_ctx* h, const mfa_kv* kv, int32_t batch, const cha
             return fail(MFA_ERR_INVALID, "%s: kv_stride %lld < max_seq_len %d", fn, (long long)kv->kv_stride, ml);
     }
     if (h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3) {
-        if (!(kv->k_scale > 0.f) || !isfinite(kv->k_scale) || !(kv->v_scale > 0.f) || !isfinite(kv->v_scale))
+        const float vs = h->cfg.kv_latent ? kv->k_scale : kv->v_scale;   // a latent row is key and value
+        if (!(kv->k_scale > 0.f) || !isfinite(kv->k_scale) || !(vs > 0.f) || !isfinite(vs))
             return fail(MFA_ERR_INVALID, "%s: FP8 scales must be finite and > 0 (k %g, v %g)", fn,
                         (double)kv->k_scale, (double)kv->v_scale);
     }
@@ -459,10 +478,47 @@ static mfa::KvView make_view(const mfa_ctx* h, const mfa_kv* kv, int32_t max_len
     v.page_table = h->cfg.page_size ? kv->page_table : nullptr;
     v.kv_stride = kv->kv_stride;
     v.pt_stride = kv->pt_stride;
-    v.row_bytes = mfa::kHeadDim * (h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3 ? 1 : 2);
+    v.row_bytes = (h->cfg.kv_latent ? mfa::kLatent : mfa::kHeadDim) * (h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3 ? 1 : 2);
     v.max_len = max_len;
     v.groups = h->cfg.kv_heads;
     return v;
+}
+
+// Latent-cache mode: one query token per sequence, chunks of latent_chunk
+// tokens, partials merged by a second launch when a sequence has several.
+static int decode_latent(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t max_len, void* out, float* lse_out,
+                         int32_t batch, int32_t qtok, void* hip_stream, const char* fn) {
+    if (qtok != 1) return fail(MFA_ERR_UNSUPPORTED, "%s: a latent-cache handle decodes one token per sequence", fn);
+    mfa::AttnArgs a{};
+    a.q = (const uint16_t*)q;
+    a.kv = make_view(h, kv, max_len);
+    a.out = (uint16_t*)out;
+    a.lse_out = lse_out;
+    a.part_o = h->part_o;
+    a.part_lse = h->part_lse;
+    a.counters = h->counters;
+    a.batch = batch;
+    a.qtok = 1;
+    a.nh = 2;
+    a.kv_groups = 1;
+    a.chunk = h->cfg.split_tokens > 0 ? h->cfg.split_tokens : latent_chunk(h, batch, max_len);
+    a.n_chunk = std::max<int32_t>(1, (max_len + a.chunk - 1) / a.chunk);
+    if (a.n_chunk > h->max_chunks)
+        return fail(MFA_ERR_INVALID, "%s: %d chunks exceed the workspace (%d)", fn, a.n_chunk, h->max_chunks);
+    a.part_stride = a.n_chunk;
+    if ((int64_t)batch * a.n_chunk > h->part_slots)
+        return fail(MFA_ERR_UNSUPPORTED, "%s: %d rows x %d partial slots exceed the workspace's %lld", fn, batch,
+                    a.n_chunk, (long long)h->part_slots);
+    const float log2e = 1.4426950408889634f;
+    a.score_scale = h->cfg.softmax_scale * kv->k_scale * log2e;
+    a.v_scale = kv->k_scale;
+    hipStream_t st = (hipStream_t)hip_stream;
+    const bool paged = h->cfg.page_size != 0;
+    hipError_t e = timed_launch(h, MFA_KERNEL_ATTENTION, st, [&](const mfa::Launch& l) { return mfa::launch_mla(a, paged, l); });
+    if (e == hipSuccess && a.n_chunk > 1)
+        e = timed_launch(h, MFA_KERNEL_COMBINE, st, [&](const mfa::Launch& l) { return mfa::launch_mla_combine(a, l); });
+    if (e != hipSuccess) return hip_fail(e, (std::string(fn) + ": launch").c_str());
+    return MFA_OK;
 }
 
 // mfa_decode (qtok 1) and mfa_decode_mtp (qtok query tokens per sequence).
@@ -483,6 +539,7 @@ static int decode_impl(mfa_ctx* h, const void* q, const mfa_kv* kv, int32_t qtok
         return fail(MFA_ERR_INVALID, "%s: batch %d x num_tokens %d exceeds max_batch %d", fn, batch, qtok,
                     h->cfg.max_batch);
     const bool fp8 = h->cfg.kv_dtype == MFA_DTYPE_FP8_E4M3;
+    if (h->cfg.kv_latent) return decode_latent(h, q, kv, max_len, out, lse_out, batch, qtok, hip_stream, fn);
     mfa::AttnArgs a;
     a.q = (const uint16_t*)q;
     a.kv = make_view(h, kv, max_len);
@@ -594,6 +651,7 @@ int mfa_decode_noalloc(const mfa_config* cfg, const void* q, const mfa_kv* kv, v
     mfa_config c;
     int rc = validate_config(cfg, &c, "mfa_decode_noalloc");
     if (rc) return rc;
+    if (c.kv_latent) return fail(MFA_ERR_UNSUPPORTED, "mfa_decode_noalloc: not for a latent cache");
     if ((int64_t)c.max_batch * 4 * 4 > (int64_t)kNoAllocCounterBytes)
         return fail(MFA_ERR_UNSUPPORTED, "mfa_decode_noalloc: max_batch %d exceeds the scratch's %d", c.max_batch,
                     (int)(kNoAllocCounterBytes / 16));
@@ -622,7 +680,8 @@ int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v,
                   int32_t batch, void* hip_stream) {
     g_last_error[0] = 0;
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_kv_append: not a live handle");
-    if (h->cfg.kv_heads > 1) return fail(MFA_ERR_UNSUPPORTED, "mfa_kv_append: needs kv_heads 1");
+    if (h->cfg.kv_heads > 1 || h->cfg.kv_latent)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_kv_append: needs kv_heads 1 and no latent cache");
     if (!x || !w_k || !w_v) return fail(MFA_ERR_INVALID, "mfa_kv_append: null x, w_k or w_v");
     int32_t max_len = 0;
     int rc = check_kv(h, kv, batch, "mfa_kv_append", &max_len);
@@ -659,7 +718,8 @@ int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, 
                         void* hip_stream) {
     g_last_error[0] = 0;
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_debug_gather_kv: not a live handle");
-    if (h->cfg.kv_heads > 1) return fail(MFA_ERR_UNSUPPORTED, "mfa_debug_gather_kv: needs kv_heads 1");
+    if (h->cfg.kv_heads > 1 || h->cfg.kv_latent)
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_debug_gather_kv: needs kv_heads 1 and no latent cache");
     if (!k_dst || !v_dst) return fail(MFA_ERR_INVALID, "mfa_debug_gather_kv: null destination");
     int32_t max_len = 0;
     int rc = check_kv(h, kv, h->cfg.max_batch, "mfa_debug_gather_kv", &max_len);

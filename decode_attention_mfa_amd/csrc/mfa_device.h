@@ -25,6 +25,7 @@ constexpr int kHeads = 64;      // query heads sharing one K/V head
 constexpr int kHeadDim = 256;   // head dimension of Q, K and V
 constexpr int kPage = 64;       // tokens per cache page
 constexpr int kStep = 64;       // tokens per attention step (one page)
+constexpr int kLatent = 512;    // latent row of the latent-cache (MLA-style) comparison mode
 constexpr float kLn2 = 0.69314718055994530942f;
 // Headroom (base-2 exponent) a score may exceed its head's reference maximum
 // before the chunk is redone with a higher reference: unnormalised P stays

@@ -74,6 +74,11 @@ constexpr int kMaxPagedChunkSteps = kMaxPieceSteps;
 
 hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgroups, const Launch& l);
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l);
+// Latent-cache mode (mfa_mla.hip): q, out [batch][64][512]; kv.k holds the
+// E4M3 latent rows; chunks of a.chunk tokens, two workgroups of 32 heads per
+// (row, chunk); partials in 64 KB workspace slots, merged by the second launch
+hipError_t launch_mla(const AttnArgs& a, bool paged, const Launch& l);
+hipError_t launch_mla_combine(const AttnArgs& a, const Launch& l);
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
                          void* v_dst, const Launch& l);
 // n 32-bit words at p set to zero by a kernel (capturable in a graph, unlike

@@ -49,6 +49,7 @@ class DeviceCase:
     split_tokens: int = 0
     min_len: int = 0             # lower bound of the lengths (as a scheduler knows it), 0 = unknown
     kv_heads: int = 1            # K/V heads per token (grouped-query caches: 2 or 4)
+    kv_latent: int = 0           # 512: latent-cache mode (q, out [B, 64, 512])
 
     @property
     def paged(self) -> bool:
@@ -71,7 +72,7 @@ def to_device(case, device="cuda") -> DeviceCase:
         w_k=_dev(getattr(case, "w_k", None), device), w_v=_dev(getattr(case, "w_v", None), device),
         softmax_scale=case.softmax_scale, rms_eps=case.rms_eps, split_tokens=case.split_tokens,
         min_len=max(0, int(case.seq_lens.min())) if case.batch else 0,
-        kv_heads=getattr(case, "kv_heads", 1))
+        kv_heads=getattr(case, "kv_heads", 1), kv_latent=getattr(case, "kv_latent", 0))
 
 
 def create_handle(dc: DeviceCase, *, max_batch: Optional[int] = None, max_context: Optional[int] = None,
@@ -82,11 +83,11 @@ def create_handle(dc: DeviceCase, *, max_batch: Optional[int] = None, max_contex
         max_context=max_context or dc.max_len,
         split_tokens=dc.split_tokens if split_tokens is None else split_tokens,
         rms_eps=dc.rms_eps, softmax_scale=dc.softmax_scale, attn_math=attn_math,
-        kv_heads=dc.kv_heads))
+        kv_heads=dc.kv_heads, kv_latent=dc.kv_latent))
 
 
 def alloc_outputs(dc: DeviceCase):
-    out = torch.empty((dc.batch, HEADS, HEAD_DIM), dtype=torch.int16, device=dc.k.device)
+    out = torch.empty((dc.batch, HEADS, dc.kv_latent or HEAD_DIM), dtype=torch.int16, device=dc.k.device)
     lse = torch.empty((dc.batch, HEADS), dtype=torch.float32, device=dc.k.device)
     return out, lse
 

@@ -109,6 +109,18 @@ typedef struct {
                               MFA_ATTN_BF16_MFMA (bf16 or FP8 cache); mfa_decode only (not
                               mfa_decode_mtp, mfa_kv_append or mfa_debug_gather_kv) and not
                               MFA_SPLIT_BALANCED (else MFA_ERR_UNSUPPORTED) */
+    int32_t kv_latent;     /* 0: MFA's K and V heads. 512: latent-cache mode, for comparing
+                              head-sharing schemes with an MLA-style cache (the Step-3
+                              Key points' ablation names MLA; this is the library's reading
+                              of it, the pages give no latent shape): every token stores
+                              ONE 512-wide E4M3 latent row c_t (kv.k; kv.v unused, may be
+                              NULL; value = decode(code) * kv.k_scale) that all 64 heads
+                              use as key and as value, the key and value up-projections
+                              being absorbed into the query and the output projection:
+                              q and out are [batch][64][512] bf16, s_ht = softmax_scale *
+                              <q_h, c_t>, out_h = sum_t softmax_t(s_h) c_t. Needs an FP8
+                              cache, kv_heads 1, MFA_ATTN_BF16_MFMA and chunked splits;
+                              mfa_decode only (else MFA_ERR_UNSUPPORTED) */
 } mfa_config;
 
 /* KV cache of one layer for one call (host struct describing device buffers).
@@ -120,6 +132,8 @@ typedef struct {
  *   With G = kv_heads > 1: contiguous [batch][G][kv_stride][256] (head g of
  *     token t at row (b * G + g) * kv_stride + t); paged pools
  *     [num_pages][G][64][256] (row (page * G + g) * 64 + t % 64).
+ * Latent-cache handles (kv_latent 512): k holds 512-byte rows in the same
+ *   layouts ([batch][kv_stride][512] or pools [num_pages][64][512]).
  * Element type: bf16 or E4M3 per the handle's kv_dtype. An FP8 element's
  * value is decode(code) * k_scale (keys) or * v_scale (values). Only rows
  * t < seq_lens[b] are read; mfa_kv_append writes row seq_lens[b]. */
@@ -189,7 +203,11 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w,
  * else by a second kernel on the same stream. The result depends only on the
  * logical K/V values, the lengths and the chunking, not on the cache layout:
  * paged and contiguous caches holding the same rows give bitwise equal
- * outputs. 1 <= batch <= max_batch. */
+ * outputs. 1 <= batch <= max_batch.
+ * Latent-cache handles (mfa_config.kv_latent = 512): q and out are
+ * [batch][64][512] bf16, kv.k the latent rows; two workgroups of 32 heads per
+ * (sequence, chunk), chunks of split_tokens or of the per-call choice; a
+ * sequence with several chunks is merged by a second kernel. */
 int mfa_decode(mfa_handle h, const void* q, const mfa_kv* kv, void* out, float* lse_out,
                int32_t batch, void* hip_stream);
 

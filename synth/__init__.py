@@ -104,6 +104,7 @@ class Case:
     w_v: Optional[np.ndarray] = None
     softmax_scale: float = 1.0 / 16.0
     rms_eps: float = 1e-6
+    kv_latent: int = 0             # 512: latent-cache case (k = v = latent rows [., 512], q [B, 64, 512])
     split_tokens: int = 0
     seed: int = 0
     kv_heads: int = 1
@@ -257,6 +258,42 @@ def gqa_case(kv_heads: int, *, batch: Optional[int] = None, scale_len: float = 1
     seed = 1003 if kv_heads == 1 else 1100 + kv_heads
     return make_case(f"fp8_gqa{kv_heads}", B, max(1, int(4096 * scale_len)), "fp8", seed=seed,
                      paged=paged, kv_heads=kv_heads)
+
+
+LATENT = 512
+
+
+def latent_case(name: str, batch: int, seq_lens, *, seed: int = 0, paged: bool = False, kv_slack: int = 0,
+                q_std: float = 1.0, split_tokens: int = 0) -> Case:
+    """A latent-cache (MLA-style) case: one 512-wide latent row per token,
+    N(0,1) encoded to E4M3 with a per-tensor amax scale, serving as key and
+    value of all 64 heads (k and v are the same array); Q [B, 64, 512] bf16
+    N(0, q_std). Contiguous [B, max(L) + kv_slack, 512] or pages [P, 64, 512]
+    with the page table of make_case."""
+    st = _streams(seed)
+    L = np.broadcast_to(np.asarray(seq_lens, dtype=np.int32), (batch,)).copy()
+    maxL = int(L.max()) if batch else 0
+    case = Case(name=name, batch=batch, kv_dtype="fp8", seq_lens=L, k=None, v=None, seed=seed,
+                split_tokens=split_tokens, kv_latent=LATENT)
+    if paged:
+        npg = (L.astype(np.int64) + PAGE_SIZE - 1) // PAGE_SIZE
+        P = int(npg.sum())
+        pt_stride = max(1, (maxL + PAGE_SIZE - 1) // PAGE_SIZE)
+        perm = st["perm"].permutation(P).astype(np.int32)
+        pt = np.zeros((batch, pt_stride), dtype=np.int32)
+        off = 0
+        for b in range(batch):
+            n = int(npg[b])
+            pt[b, :n] = perm[off:off + n]
+            off += n
+        case.page_table = pt
+        shape = (max(P, 1), PAGE_SIZE, LATENT)
+    else:
+        shape = (batch, maxL + kv_slack, LATENT)
+    case.k, case.k_scale = _kv_tensor(st["k"], shape, "fp8")
+    case.v, case.v_scale = case.k, case.k_scale
+    case.q = bf16_bits(_normal(st["q"], (batch, NUM_HEADS, LATENT), q_std))
+    return case
 
 
 def _with_append(base: Case) -> Case:

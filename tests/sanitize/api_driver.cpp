@@ -110,6 +110,9 @@ static void bad_configs() {
         {[](mfa_config& c) { c.kv_heads = 2; c.attn_math = MFA_ATTN_FP8_MFMA; }, MFA_ERR_UNSUPPORTED},
         {[](mfa_config& c) { c.kv_heads = 4; c.split_tokens = MFA_SPLIT_BALANCED; }, MFA_ERR_UNSUPPORTED},
         {[](mfa_config& c) { c.max_batch = 1 << 30; c.max_context = 1 << 30; }, MFA_ERR_INVALID},
+        {[](mfa_config& c) { c.kv_latent = 256; }, MFA_ERR_INVALID},
+        {[](mfa_config& c) { c.kv_latent = 512; c.kv_dtype = MFA_DTYPE_BF16; }, MFA_ERR_UNSUPPORTED},
+        {[](mfa_config& c) { c.kv_latent = 512; c.split_tokens = MFA_SPLIT_BALANCED; }, MFA_ERR_UNSUPPORTED},
     };
     for (const Case& k : cases) {
         mfa_config b = base_config();
@@ -147,7 +150,7 @@ static void sweep(const mfa_config& c) {
                 EXPECT(st >= 0 && st % 64 == 0, "split tokens %d", st);
                 EXPECT(hg >= 1 && hg <= 4, "head groups %d", hg);
                 if (G > 1) EXPECT(hg == G, "grouped head groups %d", hg);
-                if (G == 1 && c.attn_math == MFA_ATTN_BF16_MFMA) {
+                if (G == 1 && c.attn_math == MFA_ATTN_BF16_MFMA && !c.kv_latent) {
                     for (int t : {2, 3, 4, 16}) {
                         const int want = batch * t <= c.max_batch ? MFA_OK : MFA_ERR_INVALID;
                         rc = mfa_decode_mtp(h, g_dummy, &kv.kv, t, g_dummy, nullptr, batch, nullptr);
@@ -156,14 +159,14 @@ static void sweep(const mfa_config& c) {
                 }
                 if (G == 1) {
                     rc = mfa_kv_append(h, g_dummy, g_dummy, g_dummy, &kv.kv, batch, nullptr);
-                    EXPECT(rc == MFA_OK, "append batch %d: %d", batch, rc);
+                    EXPECT(rc == (c.kv_latent ? MFA_ERR_UNSUPPORTED : MFA_OK), "append batch %d: %d", batch, rc);
                 }
                 rc = mfa_decode_noalloc(&c, g_dummy, &kv.kv, g_dummy, nullptr, batch, nullptr);
                 EXPECT(rc == MFA_OK || rc == MFA_ERR_UNSUPPORTED, "noalloc batch %d max %d: %d", batch, ml, rc);
             }
         }
         rc = mfa_qproj(h, g_dummy, g_dummy, g_dummy, g_dummy, g_dummy, batch, nullptr);
-        EXPECT(rc == MFA_OK, "qproj batch %d: %d", batch, rc);
+        EXPECT(rc == (c.kv_latent ? MFA_ERR_UNSUPPORTED : MFA_OK), "qproj batch %d: %d", batch, rc);
     }
     // rejections on a live handle
     Kv kv = make_kv(c, 4, 100, 0);
@@ -206,12 +209,13 @@ static void sweep(const mfa_config& c) {
         bad.k_scale = 0.f;
         EXPECT(mfa_decode(h, g_dummy, &bad, g_dummy, nullptr, 4, nullptr) == MFA_ERR_INVALID, "zero k_scale");
         bad = kv.kv;
-        bad.v_scale = __builtin_inff();
-        EXPECT(mfa_decode(h, g_dummy, &bad, g_dummy, nullptr, 4, nullptr) == MFA_ERR_INVALID, "inf v_scale");
+        bad.v_scale = __builtin_inff();   // ignored by a latent cache (its rows are keys and values)
+        EXPECT(mfa_decode(h, g_dummy, &bad, g_dummy, nullptr, 4, nullptr) == (c.kv_latent ? MFA_OK : MFA_ERR_INVALID),
+               "inf v_scale");
     }
-    EXPECT(mfa_qproj(h, nullptr, g_dummy, g_dummy, g_dummy, g_dummy, 1, nullptr) == MFA_ERR_INVALID, "qproj null");
+    EXPECT(mfa_qproj(h, nullptr, g_dummy, g_dummy, g_dummy, g_dummy, 1, nullptr) < 0, "qproj null");
     EXPECT(mfa_kv_append(h, g_dummy, nullptr, g_dummy, &kv.kv, 1, nullptr) != MFA_OK, "append null");
-    if (G == 1) {
+    if (G == 1 && !c.kv_latent) {
         EXPECT(mfa_debug_gather_kv(h, &kv.kv, 0, g_dummy, g_dummy, nullptr) == MFA_OK, "gather");
         EXPECT(mfa_debug_gather_kv(h, &kv.kv, c.max_batch, g_dummy, g_dummy, nullptr) == MFA_ERR_INVALID,
                "gather b out of range");
@@ -338,6 +342,15 @@ int main(int argc, char** argv) {
                             sweep(c);
                         }
                 }
+        for (int page : {0, 64})   // latent-cache handles
+            for (int split : {0, 256, 1024}) {
+                mfa_config c = base_config();
+                c.kv_dtype = MFA_DTYPE_FP8_E4M3;
+                c.page_size = page;
+                c.split_tokens = split;
+                c.kv_latent = 512;
+                sweep(c);
+            }
         for (int cu : {1, 8, 80, 304}) {   // planning for other compute-unit counts
             stub_set_num_cu(cu);
             mfa_config c = base_config();

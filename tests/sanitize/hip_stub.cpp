@@ -167,6 +167,22 @@ hipError_t launch_attn_split(const AttnArgs& a, bool, bool paged, int workgroups
     g_launches++;
     return hipSuccess;
 }
+hipError_t launch_mla(const AttnArgs& a, bool paged, const Launch&) {
+    if (paged != (a.kv.page_table != nullptr)) die("launch_mla: paged flag", a.kv.page_table, 0);
+    if (a.chunk <= 0 || a.chunk % kStep || (int64_t)a.chunk * a.n_chunk < a.kv.max_len)
+        die("launch_mla: chunks do not cover max_len", nullptr, (size_t)a.chunk);
+    const int64_t slots = (int64_t)a.batch * a.n_chunk;
+    need("launch_mla part_o", a.part_o, (size_t)slots * kHeads * kLatent * 2);
+    need("launch_mla part_lse", a.part_lse, (size_t)slots * kHeads * 4);
+    g_launches++;
+    return hipSuccess;
+}
+hipError_t launch_mla_combine(const AttnArgs& a, const Launch&) {
+    const int64_t slots = (int64_t)a.batch * a.n_chunk;
+    need("launch_mla_combine part_o", a.part_o, (size_t)slots * kHeads * kLatent * 2);
+    g_launches++;
+    return hipSuccess;
+}
 hipError_t launch_combine(const AttnArgs& a, int rows, const Launch&) {
     check_attn(a, rows, "launch_combine");
     g_launches++;

@@ -58,6 +58,11 @@ def _create(**kw):
     (dict(kv_heads=8, kv_dtype="fp8"), -1, "kv_heads"),
     (dict(kv_heads=2, kv_dtype="fp8", attn_math=1), -2, "kv_heads > 1"),
     (dict(kv_heads=4, kv_dtype="fp8", split_tokens=-1), -2, "kv_heads > 1"),
+    (dict(kv_latent=256, kv_dtype="fp8"), -1, "kv_latent"),
+    (dict(kv_latent=512, kv_dtype="bf16"), -2, "kv_latent"),
+    (dict(kv_latent=512, kv_dtype="fp8", kv_heads=2), -2, "kv_latent"),
+    (dict(kv_latent=512, kv_dtype="fp8", split_tokens=-1), -2, "kv_latent"),
+    (dict(kv_latent=512, kv_dtype="fp8", attn_math=1), -2, "kv_latent"),
 ])
 def test_create_rejects_bad_config(kw, status, needle):
     st, msg, h = _create(**kw)
