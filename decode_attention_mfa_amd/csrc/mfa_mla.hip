@@ -13,17 +13,17 @@
 // With an FP8 latent a token costs the same 512 cache bytes as MFA's K and V
 // rows, and twice MFA's matrix work: the comparison isolates the arithmetic.
 //
-// One workgroup (four waves) takes 32 of the 64 heads of one (sequence,
+// One workgroup (eight waves) takes 32 of the 64 heads of one (sequence,
 // chunk); the two head groups of a (sequence, chunk) get block indices 8
 // apart in a group of 16, so that the round-robin dispatch puts them on one
 // XCD, where the second reads the latent rows from L2. Per 64-token step the
-// latent tile (32 KB of E4M3 codes) streams into a three-slot LDS ring by
-// direct DMA; each wave scores 16 tokens against the 32 heads (bf16 MFMAs on
-// the widened codes, Q held in registers), the softmax keeps a running
-// maximum per head and rescales the output accumulators when it rises, and
-// each wave then accumulates 128 of the 512 output columns for the 32 heads
-// from the transposed tile (the same LDS bytes the scores read). Two
-// barriers per step. Pieces are merged by mfa_mla_combine_kernel.
+// latent tile (32 KB of E4M3 codes) streams into a four-slot LDS ring by
+// direct DMA; each wave scores 16 tokens against 16 heads (bf16 MFMAs on the
+// widened codes, Q held in registers), the softmax keeps a running maximum
+// per head and rescales the output accumulators when it rises, and each wave
+// then accumulates 64 of the 512 output columns for the 32 heads from the
+// transposed tile (the same LDS bytes the scores read). Two barriers per
+// step; two waves per SIMD overlap each other's MFMA and VALU work. Pieces are merged by mfa_mla_combine_kernel.
 #include "mfa_device.h"
 #include "mfa_internal.h"
 
@@ -33,9 +33,9 @@ namespace {
 
 constexpr int kRowB = kLatent;          // bytes per FP8 latent row
 constexpr int kSlot = kStep * kRowB;    // one step's tile: 32 KB
-constexpr int kRing = 3;                // tiles in the ring
+constexpr int kRing = 4;                // tiles in the ring
 constexpr int kHg = 32;                 // heads per workgroup
-constexpr int kDmaPerStep = kSlot / (256 * 16);   // 16-byte DMA instructions per thread and step (8)
+constexpr int kDmaPerStep = kSlot / (512 * 16);   // 16-byte DMA instructions per thread and step (4)
 
 // 16-byte chunk c of row r of a tile sits at chunk position c ^ (r & 31): the
 // score reads (16 rows, one chunk column) and the transposed reads (8 rows)
@@ -79,18 +79,23 @@ __device__ __forceinline__ const uint8_t* mla_uniform(const uint8_t* ptr) {
 
 }  // namespace
 
-// Grid: round_up(batch * n_chunk, 8) * 2 blocks of 256 threads. Block x:
-// work item wi = 8 (x / 16) + x % 8 is (row b, chunk c) = (wi / n_chunk,
-// wi % n_chunk); head group (x % 16) / 8 takes heads 32 hg .. 32 hg + 31.
+// Grid: round_up(batch * n_chunk, 8) * 2 blocks of 512 threads (eight
+// waves, two per SIMD, so that one wave's MFMAs run while the other does its
+// VALU work or waits). Block x: work item wi = 8 (x / 16) + x % 8 is (row b,
+// chunk c) = (wi / n_chunk, wi % n_chunk); head group hg = (x % 16) / 8
+// takes heads 32 hg .. 32 hg + 31. Wave v scores tokens 16 (v % 4) .. +15
+// of each step against head tile v / 4 (16 heads) and accumulates output
+// columns 64 v .. 64 v + 63 of all 32 heads.
 template <bool PAGED>
-__global__ __launch_bounds__(256) void mfa_mla_kernel(const AttnArgs p) {
+__global__ __launch_bounds__(512) void mfa_mla_kernel(const AttnArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kRing * kSlot];
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[kHg * kStep * 2];
-    __shared__ float xmax[4][kHg];
-    __shared__ float xsum[4][kHg];
+    __shared__ float xmax[4][kHg];   // [token block][head]: the block's maximum
+    __shared__ float xsum[4][kHg];   // [token block][head]: the block's share of the sum of P
 
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int v = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tw = v & 3, ht = v >> 2;   // score role: token block, head tile
     const int l = tid & 63, lr = l & 15, g = l >> 4;
     const int grp = blockIdx.x >> 4, r16 = blockIdx.x & 15;
     const int wi = grp * 8 + (r16 & 7);
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(256) void mfa_mla_kernel(const AttnArgs p) {
     uint16_t* const ob = p.out + ((int64_t)b * kHeads + hb) * kLatent;   // this group's 32 output rows
     if (t_begin >= L) {
         if (c == 0) {   // empty sequence: out = 0, lse = -inf
-            for (int i = tid; i < kHg * kLatent / 8; i += 256) reinterpret_cast<u32x4*>(ob)[i] = u32x4{0, 0, 0, 0};
+            for (int i = tid; i < kHg * kLatent / 8; i += 512) reinterpret_cast<u32x4*>(ob)[i] = u32x4{0, 0, 0, 0};
             if (p.lse_out && tid < kHg) p.lse_out[b * kHeads + hb + tid] = -__builtin_inff();
         }
         return;
@@ -130,11 +135,11 @@ __global__ __launch_bounds__(256) void mfa_mla_kernel(const AttnArgs p) {
         const uint32_t slot = lds_u32(ring + (s % kRing) * kSlot);
 #pragma unroll
         for (int i = 0; i < kDmaPerStep; i++) {
-            // instruction i of wave w fills rows 8 i + 2 w + l / 32, chunk position l % 32
-            const int row = 8 * i + 2 * w + (l >> 5);
+            // instruction i of wave v fills rows 16 i + 2 v + l / 32, chunk position l % 32
+            const int row = 16 * i + 2 * v + (l >> 5);
             const int srow = min(row, last);
             const uint32_t voff = (uint32_t)(srow * kRowB + 16 * ((l & 31) ^ lswz(row)));
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(slot + 4096 * i + 1024 * w);
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(slot + 8192 * i + 1024 * v);
             if (i == 0)
                 mla_dma_first(src, voff, dst);
             else
@@ -142,104 +147,107 @@ __global__ __launch_bounds__(256) void mfa_mla_kernel(const AttnArgs p) {
         }
     };
 
-    f32x4 o[2][8];
+    f32x4 o[2][4];   // O[16 h2 + 4 g + i][64 v + 16 dt + lr]
 #pragma unroll
-    for (int ht = 0; ht < 2; ht++)
+    for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-        for (int dt = 0; dt < 8; dt++) o[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-__builtin_inff(), -__builtin_inff()};   // running maximum of head 16 ht + lr (base 2)
-    float l_run[2] = {0.f, 0.f};                                // this lane's share of its sum of P
+        for (int dt = 0; dt < 4; dt++) o[h2][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-__builtin_inff(), -__builtin_inff()};   // running maximum of head 16 h2 + lr (base 2)
+    float l_run = 0.f;   // this lane's share of the sum of P of head 16 ht + lr
 
-    issue(0);
-    issue(1);
-    // Q as MFMA B operands: qop[ht][ks] = q[hb + 16 ht + lr][32 ks + 8 g + 0..7]
-    // (loaded after the ring's first DMA, so the waits for them also cover it)
-    bf16x8 qop[2][16];
+    // Q of head tile ht as MFMA B operands: qop[ks] = q[hb + 16 ht + lr][32 ks + 8 g + 0..7]
+    // (loaded before the ring's first DMA: the compiler's waits for them then
+    // do not wait for the ring)
+    bf16x8 qop[16];
     {
-        const uint16_t* qb = p.q + ((int64_t)b * kHeads + hb) * kLatent;
+        const uint16_t* qb = p.q + ((int64_t)b * kHeads + hb + 16 * ht + lr) * kLatent;
 #pragma unroll
-        for (int ht = 0; ht < 2; ht++)
-#pragma unroll
-            for (int ks = 0; ks < 16; ks++)
-                qop[ht][ks] = *reinterpret_cast<const bf16x8*>(qb + (16 * ht + lr) * kLatent + 32 * ks + 8 * g);
+        for (int ks = 0; ks < 16; ks++) qop[ks] = *reinterpret_cast<const bf16x8*>(qb + 32 * ks + 8 * g);
     }
+    for (int s = 0; s < kRing - 1; s++) issue(s);
+    // tile 0 has landed once at most the two younger tiles' loads are in
+    // flight; the barrier shows every thread's part
+    mla_wait_vmem<2 * kDmaPerStep>();
+    mla_lds_barrier();
     for (int s = 0; s < nsteps; s++) {
-        // this thread's part of tile s has landed once at most the next
-        // step's loads are in flight; the barrier shows every thread's part
-        // and retires step s - 1 (its tile slot and P)
-        mla_wait_vmem<kDmaPerStep>();
-        mla_lds_barrier();
-        issue(s + 2);
         const uint8_t* const tile = ring + (s % kRing) * kSlot;
 
-        // scores of tokens 16 w + 4 g + i against heads 16 ht + lr
-        f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        // scores of tokens 16 tw + 4 g + i against heads 16 ht + lr
+        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
         {
-            const int row = 16 * w + lr;
+            const int row = 16 * tw + lr;
 #pragma unroll
             for (int ks = 0; ks < 16; ks++) {
                 const int ch = 2 * ks + (g >> 1);
                 const u32x2 kk = *reinterpret_cast<const u32x2*>(tile + row * kRowB + 16 * (ch ^ lswz(row)) + 8 * (g & 1));
-                const bf16x8 ka = e4m3x8_to_bf16x8(kk.x, kk.y);
-                sc[0] = mfma16(ka, qop[0][ks], sc[0]);
-                sc[1] = mfma16(ka, qop[1][ks], sc[1]);
+                sc = mfma16(e4m3x8_to_bf16x8(kk.x, kk.y), qop[ks], sc);
             }
         }
-        const int tq = t_begin + s * kStep + 16 * w + 4 * g;   // token of element i = 0
+        const int tq = t_begin + s * kStep + 16 * tw + 4 * g;   // token of element i = 0
 #pragma unroll
-        for (int ht = 0; ht < 2; ht++) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) sc[ht][i] = tq + i < t_end ? sc[ht][i] * p.score_scale : -__builtin_inff();
-            float m = fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3]));
+        for (int i = 0; i < 4; i++) sc[i] = tq + i < t_end ? sc[i] * p.score_scale : -__builtin_inff();
+        {
+            float m = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
             m = fmaxf(m, __shfl_xor(m, 16));
             m = fmaxf(m, __shfl_xor(m, 32));
-            if (g == 0) xmax[w][16 * ht + lr] = m;
+            if (g == 0) xmax[tw][16 * ht + lr] = m;
         }
-        mla_lds_barrier();   // barrier A: every wave's maxima
+        // barrier A: every token block's maxima; every wave is done with step
+        // s - 1 (its P and its tile slot, which the loads of step s + 3 refill)
+        mla_lds_barrier();
+        issue(s + kRing - 1);
         float alpha[2];
 #pragma unroll
-        for (int ht = 0; ht < 2; ht++) {
-            const int h = 16 * ht + lr;
+        for (int h2 = 0; h2 < 2; h2++) {
+            const int h = 16 * h2 + lr;
             const float ms = fmaxf(fmaxf(xmax[0][h], xmax[1][h]), fmaxf(xmax[2][h], xmax[3][h]));
-            const float mn = fmaxf(m_run[ht], ms);
-            alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - mn);   // 0 on the first step
-            m_run[ht] = mn;
+            const float mn = fmaxf(m_run[h2], ms);
+            alpha[h2] = __builtin_amdgcn_exp2f(m_run[h2] - mn);   // 0 on the first step
+            m_run[h2] = mn;
+        }
+        {
+            const float mh = ht ? m_run[1] : m_run[0];
+            const float ah = ht ? alpha[1] : alpha[0];
             float ps[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) ps[i] = __builtin_amdgcn_exp2f(sc[ht][i] - mn);
-            l_run[ht] = l_run[ht] * alpha[ht] + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
-            // P[h][tok] as bf16, tok = 16 w + 4 g + i: chunk 2 w + g / 2, elements 4 (g % 2) + i
-            const u32x2 pk = u32x2{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
-            *reinterpret_cast<u32x2*>(pbuf + h * 128 + 16 * ((2 * w + (g >> 1)) ^ pswz32(h)) + 8 * (g & 1)) = pk;
+            for (int i = 0; i < 4; i++) ps[i] = __builtin_amdgcn_exp2f(sc[i] - mh);
+            l_run = l_run * ah + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+            // P[h][tok] as bf16, tok = 16 tw + 4 g + i: chunk 2 tw + g / 2, elements 4 (g % 2) + i
+            const int h = 16 * ht + lr;
+            *reinterpret_cast<u32x2*>(pbuf + h * 128 + 16 * ((2 * tw + (g >> 1)) ^ pswz32(h)) + 8 * (g & 1)) =
+                u32x2{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])};
         }
-        // the output rows of this lane are heads 16 ht + 4 g + i: their alpha
+        // the output rows of this lane are heads 16 h2 + 4 g + i: their alpha
         // from the lanes that hold those heads
 #pragma unroll
-        for (int ht = 0; ht < 2; ht++)
+        for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const float a = __shfl(alpha[ht], 4 * g + i);
+                const float a = __shfl(alpha[h2], 4 * g + i);
 #pragma unroll
-                for (int dt = 0; dt < 8; dt++) o[ht][dt][i] *= a;
+                for (int dt = 0; dt < 4; dt++) o[h2][dt][i] *= a;
             }
-        mla_lds_barrier();   // barrier B: P visible
+        // barrier B: P visible, and tile s + 1 (landed once at most the two
+        // younger tiles' loads are in flight) for the next step's scores
+        mla_wait_vmem<2 * kDmaPerStep>();
+        mla_lds_barrier();
 
-        // O[16 ht + 4 g + i][128 w + 16 dt + lr] += P . C, the tile read
+        // O[16 h2 + 4 g + i][64 v + 16 dt + lr] += P . C, the tile read
         // transposed: lane j of a 16-lane group points at row r0 + j / 2,
-        // bytes 8 (j % 2) .. +7 of chunk 8 w + dt, and receives column j of
+        // bytes 8 (j % 2) .. +7 of chunk 4 v + dt, and receives column j of
         // that chunk for rows r0 .. r0 + 7
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {
             bf16x8 pa[2];
 #pragma unroll
-            for (int ht = 0; ht < 2; ht++) {
-                const int h = 16 * ht + lr;
-                pa[ht] = *reinterpret_cast<const bf16x8*>(pbuf + h * 128 + 16 * ((4 * kk + g) ^ pswz32(h)));
+            for (int h2 = 0; h2 < 2; h2++) {
+                const int h = 16 * h2 + lr;
+                pa[h2] = *reinterpret_cast<const bf16x8*>(pbuf + h * 128 + 16 * ((4 * kk + g) ^ pswz32(h)));
             }
             const int row = 32 * kk + 8 * g + (lr >> 1);
 #pragma unroll
-            for (int dt = 0; dt < 8; dt++) {
-                const uint8_t* a = tile + row * kRowB + 16 * ((8 * w + dt) ^ lswz(row)) + 8 * (lr & 1);
+            for (int dt = 0; dt < 4; dt++) {
+                const uint8_t* a = tile + row * kRowB + 16 * ((4 * v + dt) ^ lswz(row)) + 8 * (lr & 1);
                 const i32x2 vr = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(a));
                 const bf16x8 vb = e4m3x8_to_bf16x8((uint32_t)vr.x, (uint32_t)vr.y);
                 o[0][dt] = mfma16(pa[0], vb, o[0][dt]);
@@ -249,69 +257,68 @@ __global__ __launch_bounds__(256) void mfa_mla_kernel(const AttnArgs p) {
     }
     mla_wait_vmem<0>();   // the repeated loads past the last step
 
-    // ---- sums of P per head (lanes -> wave -> workgroup), normalisation
-#pragma unroll
-    for (int ht = 0; ht < 2; ht++) {
-        float v = l_run[ht];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (g == 0) xsum[w][16 * ht + lr] = v;
+    // ---- sums of P per head (lanes -> token block -> workgroup), normalisation
+    {
+        float sv = l_run;
+        sv += __shfl_xor(sv, 16);
+        sv += __shfl_xor(sv, 32);
+        if (g == 0) xsum[tw][16 * ht + lr] = sv;
     }
     __syncthreads();
 #pragma unroll
-    for (int ht = 0; ht < 2; ht++)
+    for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int h = 16 * ht + 4 * g + i;
+            const int h = 16 * h2 + 4 * g + i;
             const float tot = ((xsum[0][h] + xsum[1][h]) + xsum[2][h]) + xsum[3][h];
             const float inv = p.v_scale / tot;
 #pragma unroll
-            for (int dt = 0; dt < 8; dt++) o[ht][dt][i] *= inv;
+            for (int dt = 0; dt < 4; dt++) o[h2][dt][i] *= inv;
         }
-    // base-2 log-sum-exp of head 16 ht + lr (lanes g = 0 of wave 0 write it)
+    // base-2 log-sum-exp of head 16 h2 + lr (lanes g = 0 of wave 0 write it)
     float lse2[2];
 #pragma unroll
-    for (int ht = 0; ht < 2; ht++) {
-        const int h = 16 * ht + lr;
+    for (int h2 = 0; h2 < 2; h2++) {
+        const int h = 16 * h2 + lr;
         const float tot = ((xsum[0][h] + xsum[1][h]) + xsum[2][h]) + xsum[3][h];
-        lse2[ht] = m_run[ht] + __builtin_amdgcn_logf(tot);
+        lse2[h2] = m_run[h2] + __builtin_amdgcn_logf(tot);
     }
 
     // ---- the rows, as bf16, through LDS (ring slot 0, free now): element
     // (h, col) at byte h * 1024 + 2 * (col ^ 16 * ((h >> 2) & 3)) (the XOR
-    // spreads the four rows one ds_write_b16 covers over the banks), then 16-byte
-    // stores of whole rows: the final output for a one-piece sequence, else
-    // this piece's partial slot
+    // spreads the four rows one ds_write_b16 covers over the banks), then
+    // 16-byte stores of whole rows: the final output for a one-piece
+    // sequence, else this piece's partial slot
     uint8_t* const stage = ring;
 #pragma unroll
-    for (int ht = 0; ht < 2; ht++)
+    for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-        for (int dt = 0; dt < 8; dt++)
+        for (int dt = 0; dt < 4; dt++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const int h = 16 * ht + 4 * g + i;
-                const int col = 128 * w + 16 * dt + lr;
+                const int h = 16 * h2 + 4 * g + i;
+                const int col = 64 * v + 16 * dt + lr;
                 *reinterpret_cast<uint16_t*>(stage + h * 1024 + 2 * (col ^ (16 * ((h >> 2) & 3)))) =
-                    bitcast<uint16_t>((__bf16)o[ht][dt][i]);
+                    bitcast<uint16_t>((__bf16)o[h2][dt][i]);
             }
     __syncthreads();
     const bool single = nparts == 1;
     const int64_t pidx = (int64_t)b * p.n_chunk + c;
     uint16_t* const dst = single ? ob : reinterpret_cast<uint16_t*>(p.part_o) + (pidx * kHeads + hb) * kLatent;
 #pragma unroll
-    for (int rr = 0; rr < kHg * kLatent / 8 / 256; rr++) {
-        const int k = tid + 256 * rr, row = k >> 6, c8 = 8 * (k & 63);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * 1024 + 2 * (c8 ^ (16 * ((row >> 2) & 3))));
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + row * kLatent + c8));
+    for (int rr = 0; rr < kHg * kLatent / 8 / 512; rr++) {
+        const int k = tid + 512 * rr, row = k >> 6, c8 = 8 * (k & 63);
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * 1024 + 2 * (c8 ^ (16 * ((row >> 2) & 3))));
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst + row * kLatent + c8));
     }
-    if (w == 0 && g == 0) {
+    if (v == 0 && g == 0) {
 #pragma unroll
-        for (int ht = 0; ht < 2; ht++) {
-            const int h = hb + 16 * ht + lr;
+        for (int h2 = 0; h2 < 2; h2++) {
+            const int h = hb + 16 * h2 + lr;
             if (single) {
-                if (p.lse_out) p.lse_out[b * kHeads + h] = lse2[ht] * kLn2;
+                if (p.lse_out) p.lse_out[b * kHeads + h] = lse2[h2] * kLn2;
             } else {
-                p.part_lse[pidx * kHeads + h] = lse2[ht];
+                p.part_lse[pidx * kHeads + h] = lse2[h2];
             }
         }
     }
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(64) void mfa_mla_combine_kernel(const AttnArgs p) {
 
 hipError_t launch_mla(const AttnArgs& a, bool paged, const Launch& l) {
     const int items = (a.batch * a.n_chunk + 7) / 8 * 8;
-    const dim3 grid(2 * items), block(256);
+    const dim3 grid(2 * items), block(512);
     return paged ? launch_kernel(mfa_mla_kernel<true>, grid, block, l, a)
                  : launch_kernel(mfa_mla_kernel<false>, grid, block, l, a);
 }
