@@ -426,10 +426,17 @@ int mfa_qproj(mfa_handle h, const void* x, const void* w_qa, const void* rms_w, 
     a.hidden = h->cfg.hidden;
     a.rank = h->cfg.q_rank;
     a.nq = mfa::kHeads * mfa::kHeadDim;
-    // 1024-row K splits when they divide hidden (half the partials the last
-    // split sums), else 512
-    a.ksplit = a.hidden % (2 * mfa::kQprojRowsPerSplit) == 0 ? a.hidden / (2 * mfa::kQprojRowsPerSplit)
-                                                               : a.hidden / mfa::kQprojRowsPerSplit;
+    // K splits for the down-projection: the most that still give every
+    // workgroup its own compute unit (column blocks x row blocks x splits <=
+    // CUs), among the divisors of hidden / 64 tiles with at least 512 rows
+    // per split (the partial workspace's size)
+    {
+        const int tiles = a.hidden / 64;
+        const int blocks = (a.rank / 64) * (batch <= 32 ? 1 : (batch + 63) / 64);
+        a.ksplit = 1;
+        for (int d = 1; d <= a.hidden / mfa::kQprojRowsPerSplit; d++)
+            if (tiles % d == 0 && (int64_t)blocks * d <= h->num_cu) a.ksplit = d;
+    }
     a.eps = h->cfg.rms_eps;
     hipStream_t st = (hipStream_t)hip_stream;
     // the RMSNorm is split between the two launches (see mfa_qproj.hip)

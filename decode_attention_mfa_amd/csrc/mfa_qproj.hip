@@ -15,11 +15,12 @@
 //
 // The GEMMs have few rows (the batch) and read a large row-major [in][out]
 // weight from HBM exactly once, so they are bandwidth-bound. Each workgroup
-// owns 64 output columns and a range of K; per 64-row K tile, the weight tile
-// (64 x 64) and the matching activation tile (64 rows x 64) stream into an
-// LDS ring by direct DMA, three tiles deep (48 KB of LDS, so that several
-// workgroups share a compute unit: occupancy hides more of the load latency
-// than a deeper ring in one workgroup does). The weight tile comes back
+// (eight waves) owns 64 output columns and a range of K; per 64-row K tile,
+// the weight tile (64 x 64) and the matching activation tile (32 or 64 rows
+// x 64) stream into an LDS ring by direct DMA, three tiles deep, every wave
+// issuing part of each tile's DMA. Waves w and w + 4 own the same 16 columns
+// and take the two 32-row halves of each K tile; their sums are added
+// through LDS after the loop. The weight tile comes back
 // transposed with ds_read_b64_tr_b16 as MFMA B operands (the contraction
 // index is the weight's row), the activation tile as A operands.
 #include "mfa_device.h"
@@ -108,22 +109,26 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const void* ptr) {
 //                 sum over the block's 64 columns of c^2;
 //   kEpiBf16RowScale  bf16(acc * r[m]) in Y, r[m] = rsqrt(sum_j e.sumsq[m][j]
 //                 / e.rank + e.eps) over the e.rank / 64 column blocks j.
+constexpr int kGemmThreads = 512;   // eight waves
+
 template <int EPI, int MR>
-__global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __restrict__ X, int ldx,
+__global__ __launch_bounds__(kGemmThreads) void mfa_skinny_gemm_kernel(const uint16_t* __restrict__ X, int ldx,
                                                               const uint16_t* __restrict__ W, int N, int kper,
                                                               int M, void* __restrict__ Y,
                                                               const uint16_t* __restrict__ W2, void* __restrict__ Y2,
                                                               const GemmEpi e) {
     static_assert(MR == 32 || MR == 64, "rows per block");
     constexpr int MT = MR / 16;            // 16-row MFMA tiles
-    constexpr int XI = MR / 32;            // activation DMA instructions per wave and tile
-    constexpr int OPS = 2 + XI;            // DMA instructions per wave and tile
+    constexpr int NW = kGemmThreads / 64;  // waves
+    constexpr int XW = MR / 8;             // waves that also load 8 activation rows per tile
     constexpr int kSlot = kTileBytes + MR * 128;
     // slot: weight tile (64 rows x 128 B), then activation tile (MR rows x 128 B)
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kGemmDepth][kSlot];
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, lr = l & 15, g = l >> 4;
+    const int cw = w & 3;                  // column group: columns 16cw .. 16cw + 15
+    const int ks = w >> 2;                 // K half of every tile: rows 32ks .. 32ks + 31
     int bx = blockIdx.x;
     if (bx >= N / 64) {
         bx -= N / 64;
@@ -136,22 +141,18 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
     const int mt_n = min(MT, (M - m0 + 15) / 16);   // 16-row tiles holding real rows
     const int ntiles = kper / 64;
 
-    // DMA lane offsets (loop-invariant). Weight instruction i of wave w fills
-    // tile rows 16w + 8i + l/8, activation instruction i rows MR/4*w + 8i +
-    // l/8; lane l lands at chunk position l % 8 of its row and fetches the
-    // data chunk the swizzle puts there. Activation rows past M repeat row
-    // M-1 (in bounds; their products are never stored).
-    uint32_t woff[2], xoff[XI];
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int r = 16 * w + 8 * i + (l >> 3);
-        woff[i] = (uint32_t)(r * N * 2 + 16 * ((l & 7) ^ wswz(r)));
-    }
-#pragma unroll
-    for (int i = 0; i < XI; i++) {
-        const int r = MR / 4 * w + 8 * i + (l >> 3);
-        const int xr = min(m0 + r, M - 1) - m0;   // row within this block
-        xoff[i] = (uint32_t)(xr * ldx * 2 + 16 * ((l & 7) ^ xswz(r)));
+    // DMA lane offsets (loop-invariant). Wave w fills weight tile rows
+    // 8w + l/8 and, for w < XW, activation rows 8w + l/8; lane l lands at
+    // chunk position l % 8 of its row and fetches the data chunk the swizzle
+    // puts there. Activation rows past M repeat row M-1 (in bounds; their
+    // products are never stored).
+    const bool xload = w < XW;
+    uint32_t woff, xoff;
+    {
+        const int r = 8 * w + (l >> 3);
+        woff = (uint32_t)(r * N * 2 + 16 * ((l & 7) ^ wswz(r)));
+        const int xr = min(m0 + min(r, MR - 1), M - 1) - m0;   // row within this block
+        xoff = (uint32_t)(xr * ldx * 2 + 16 * ((l & 7) ^ xswz(r)));
     }
     // kEpiBf16RowScale: the block's rows of e.sumsq ([M][nb] fp32, nb =
     // rank/64 <= kMaxNormBlocks) are copied into LDS by 4-byte DMA ahead of the
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
     if constexpr (EPI == kEpiBf16RowScale) {
         const int nb = e.rank / 64;
         const uint8_t* sb = uniform_ptr(e.sumsq);
-        for (int i = w; i * 64 < MR * nb; i += 4) {
+        for (int i = w; i * 64 < MR * nb; i += NW) {
             const int idx = 64 * i + l;
             const int r = min(min(idx / nb, MR - 1) + m0, M - 1);
             const uint32_t off = (uint32_t)((r * nb + idx % nb) * 4);
@@ -175,12 +176,8 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
         const uint8_t* wb = uniform_ptr(W + (int64_t)k0 * N + n0);
         const uint8_t* xb = uniform_ptr(X + (int64_t)m0 * ldx + k0);
         const uint32_t slot = lds_addr_of(ring[tile % kGemmDepth]);
-        const uint32_t wdst = __builtin_amdgcn_readfirstlane(slot + 2048 * w);
-        const uint32_t xdst = __builtin_amdgcn_readfirstlane(slot + kTileBytes + MR * 32 * w);
-#pragma unroll
-        for (int i = 0; i < 2; i++) dma16_stream(wb, woff[i], wdst + 1024 * i);
-#pragma unroll
-        for (int i = 0; i < XI; i++) dma16_keep(xb, xoff[i], xdst + 1024 * i);
+        dma16_stream(wb, woff, __builtin_amdgcn_readfirstlane(slot + 1024 * w));
+        if (xload) dma16_keep(xb, xoff, __builtin_amdgcn_readfirstlane(slot + kTileBytes + 1024 * w));
     };
 
     f32x4 acc[MT];
@@ -193,15 +190,17 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
         // this wave's rows of the tile have landed once at most the younger
         // tiles' loads are in flight; the barrier shows every wave's rows and
         // frees the slot of the previous tile
-        wait_vmem<(kGemmDepth - 2) * OPS>();
+        if (xload)
+            wait_vmem<(kGemmDepth - 2) * 2>();
+        else
+            wait_vmem<(kGemmDepth - 2) * 1>();
         lds_barrier();
         issue(tile + kGemmDepth - 1);
         const uint8_t* wt = ring[tile % kGemmDepth];
         const uint8_t* xt = wt + kTileBytes;
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            // B operand: W[k = 32ks + 8g + j][n0 + 16w + lr], j = 0..7
-            const int ch = 2 * w + ((lr & 3) >> 1);
+        {
+            // B operand: W[k = 32ks + 8g + j][n0 + 16cw + lr], j = 0..7
+            const int ch = 2 * cw + ((lr & 3) >> 1);
             const int row0 = 32 * ks + 8 * g + (lr >> 2);
             const int row1 = row0 + 4;
             const i16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -222,8 +221,21 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
         }
     }
     wait_vmem<0>();   // the clamped loads past the last tile
+    // the second K half's sums (waves 4-7) join the first's through LDS,
+    // in the ring once every wave is done with it
+    __syncthreads();
+    f32x4* const red = reinterpret_cast<f32x4*>(&ring[0][0]);
+    if (ks == 1) {
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) red[(cw * MT + mt) * 64 + l] = acc[mt];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) acc[mt] += red[(cw * MT + mt) * 64 + l];
+    }
 
-    const int n = n0 + 16 * w + lr;
+    const int n = n0 + 16 * cw + lr;
     __shared__ float row_scale[MR];
     __shared__ int arrival;
     if constexpr (EPI == kEpiBf16RowScale) {
@@ -240,7 +252,7 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
     }
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
-        if (mt >= mt_n) continue;
+        if (ks != 0 || mt >= mt_n) continue;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int m = m0 + 16 * mt + 4 * g + i;
@@ -269,7 +281,7 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
         if (arrival != (int)gridDim.y - 1) return;
         if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // last split: pass pp, thread t sums columns n0 + 4(t % 16) .. +4 of
-        // row m0 + 16 pp + t / 16 over the splits, in split order, eight
+        // row m0 + 32 pp + t / 16 over the splits, in split order, eight
         // 16-byte coherent loads at a time
         const int nsplit = gridDim.y;
         const int64_t plane4 = (int64_t)M * N / 4;   // f32x4 per split plane
@@ -279,8 +291,8 @@ __global__ __launch_bounds__(256) void mfa_skinny_gemm_kernel(const uint16_t* __
         const float g0 = __builtin_bit_cast(float, gw.x << 16), g1 = __builtin_bit_cast(float, gw.x & 0xffff0000u);
         const float g2 = __builtin_bit_cast(float, gw.y << 16), g3 = __builtin_bit_cast(float, gw.y & 0xffff0000u);
 #pragma unroll
-        for (int pp = 0; pp < MR / 16; pp++) {
-            const int m = m0 + 16 * pp + (tid >> 4);
+        for (int pp = 0; pp < MR / 32; pp++) {
+            const int m = m0 + 32 * pp + (tid >> 4);
             const bool live = m < M;
             const f32x4* src = reinterpret_cast<const f32x4*>(Y) + ((int64_t)min(m, M - 1) * N + col) / 4;
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -311,10 +323,10 @@ template <int EPI>
 static hipError_t launch_skinny(int gx, int gy, const uint16_t* X, int ldx, const uint16_t* W, int N, int kper,
                                 int M, void* Y, const uint16_t* W2, void* Y2, const GemmEpi& e, const Launch& l) {
     if (M <= 32)
-        return launch_kernel(mfa_skinny_gemm_kernel<EPI, 32>, dim3(gx, gy, 1), dim3(256), l, X, ldx, W, N, kper, M,
-                             Y, W2, Y2, e);
-    return launch_kernel(mfa_skinny_gemm_kernel<EPI, 64>, dim3(gx, gy, (M + 63) / 64), dim3(256), l, X, ldx, W, N,
-                         kper, M, Y, W2, Y2, e);
+        return launch_kernel(mfa_skinny_gemm_kernel<EPI, 32>, dim3(gx, gy, 1), dim3(kGemmThreads), l, X, ldx, W, N,
+                             kper, M, Y, W2, Y2, e);
+    return launch_kernel(mfa_skinny_gemm_kernel<EPI, 64>, dim3(gx, gy, (M + 63) / 64), dim3(kGemmThreads), l, X, ldx,
+                         W, N, kper, M, Y, W2, Y2, e);
 }
 
 hipError_t launch_qproj_down(const QprojArgs& a, const Launch& l) {

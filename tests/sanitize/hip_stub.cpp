@@ -205,7 +205,8 @@ hipError_t launch_fp8_mfma(const uint8_t* a, const uint8_t* b, const float*, flo
     return hipSuccess;
 }
 hipError_t launch_qproj_down(const QprojArgs& a, const Launch&) {
-    if (a.hidden % a.ksplit || (a.hidden / a.ksplit) % kQprojRowsPerSplit) die("launch_qproj_down: ksplit", nullptr, 0);
+    if (a.ksplit < 1 || a.hidden % (64 * a.ksplit) || a.hidden / a.ksplit < kQprojRowsPerSplit)
+        die("launch_qproj_down: ksplit", nullptr, 0);
     need("launch_qproj_down c_part", a.c_part, (size_t)a.ksplit * a.batch * a.rank * 4);
     need("launch_qproj_down sumsq", a.sumsq, (size_t)a.batch * (a.rank / 64) * 4);
     need("launch_qproj_down counters", a.counters, (size_t)((a.batch + 31) / 32) * (a.rank / 64) * 4);

@@ -37,10 +37,11 @@ def _row_err(a, b):
     return float(err.max())
 
 
-@pytest.mark.parametrize("batch", [1, 5, 32, 70])
+@pytest.mark.parametrize("batch", [1, 5, 32, 48, 70])
 def test_qproj_parity_full_shape(batch):
     """hidden 7168 -> 2048 -> 64 x 256 at several batch sizes: one partial
-    16-row MFMA tile (1, 5), exact tiles (32) and two 64-row blocks (70)."""
+    16-row MFMA tile (1, 5), exact tiles (32), one 64-row block (48) and two
+    64-row blocks (70, with fewer K splits in the down-projection)."""
     m, hz = _mfa()
     case = synth.config_case(2, batch=batch, scale_len=1 / 64)
     _say(f"[qproj] B={batch} hidden=7168 rank=2048")
@@ -54,6 +55,35 @@ def test_qproj_parity_full_shape(batch):
     q_ref = oracle.case_q(case)
     e = _row_err(hz.bf16_to_f64(q), q_ref)
     _say(f"    row-rel err {e:.3e}")
+    assert e <= TOL, e
+
+
+def test_qproj_repeat_calls_bitwise():
+    """The down-projection's arrival counters return to zero after every
+    call, and its split sums do not depend on which workgroup finishes last:
+    the same inputs give the same bits on every call, across calls of other
+    batch sizes (and so other K splits) on the same handle."""
+    m, hz = _mfa()
+    case = synth.config_case(2, batch=70, scale_len=1 / 64)
+    _say(f"[qproj repeat] B=70/5/32 hidden=7168 rank=2048")
+    dc = hz.to_device(case)
+    h = hz.create_handle(dc)
+    try:
+        outs = {}
+        for b in (5, 70, 5, 32, 5, 70, 32):
+            q = torch.empty((b, 64, 256), dtype=torch.int16, device="cuda")
+            m.mfa_qproj(h, dc.x[:b].contiguous(), dc.w_qa, dc.gamma, dc.w_qb, q, b)
+            torch.cuda.synchronize()
+            outs.setdefault(b, []).append(q.cpu())
+    finally:
+        m.mfa_destroy(h)
+    for b, qs in outs.items():
+        for q in qs[1:]:
+            assert torch.equal(q, qs[0]), b
+    # the first rows do not depend on how many rows the call has
+    assert torch.equal(outs[5][0], outs[32][0][:5])
+    q_ref = oracle.case_q(case)
+    e = _row_err(hz.bf16_to_f64(outs[70][0]), q_ref)
     assert e <= TOL, e
 
 
