@@ -432,21 +432,31 @@ void mfa_attn_balanced_kernel(const AttnArgs p) {
 // Merge the chunk partials of every sequence with more than one chunk:
 //   M = max_c lse2_c, W_c = 2^(lse2_c - M), out = sum_c W_c o_c / sum_c W_c,
 //   lse = (M + log2 sum_c W_c) * ln 2.
-// One wave per (sequence, head); lane t owns columns 4t..4t+3. The chunk
-// weights go through LDS; the partial rows (bf16, 512 bytes per chunk,
-// contiguous) are read kCombineUnroll at a time so that many loads are in
-// flight. Chunks are accumulated in index order.
+// One workgroup per (sequence, head) of up to kCombineWaves waves (one per
+// kCombineUnroll chunks of the longest sequence); wave k takes the k-th of
+// equal ranges of the chunks, lane t columns 4t..4t+3.
+// The first batch of rows is loaded before the maxima are known, so that a
+// sequence of few chunks costs one memory round trip; later rows are read
+// kCombineUnroll at a time. Each wave accumulates its range in chunk order,
+// lane j holding the weight of chunk c0 + j of a 64-chunk block (broadcast
+// with readlane); the waves' sums are added in wave order.
+constexpr int kCombineWaves = 4;
 constexpr int kCombineUnroll = 16;
-constexpr int kCombineBlock = 1024;   // chunk weights staged per round
-__global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
-    __shared__ float wts[kCombineBlock];
+__global__ __launch_bounds__(64 * kCombineWaves) void mfa_combine_kernel(const AttnArgs p) {
+    __shared__ float red_m[kCombineWaves];
+    __shared__ float red_w[kCombineWaves];
+    __shared__ f32x4 red_acc[kCombineWaves][64];
     const int b = blockIdx.x >> 6;
     const int h = blockIdx.x & 63;
-    const int t = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int t = threadIdx.x & 63;
     // multi-token decode: query row b is token b % qtok of cache sequence b / qtok
     const int L = p.qtok > 1 ? max(0, seq_len(p.kv, b / p.qtok) - (p.qtok - 1 - b % p.qtok)) : seq_len(p.kv, b);
     const int nc = (L + p.chunk - 1) / p.chunk;
     if (nc <= p.fuse_max) return;   // merged by the attention kernel itself
+    const int per = (nc + nw - 1) / nw;
+    const int c_lo = min(nc, wv * per), c_hi = min(nc, c_lo + per);
     const int64_t base = (int64_t)b * p.n_chunk;
     const float* lse = p.part_lse + base * kHeads + h;   // chunk c at lse[c * kHeads]
     constexpr int64_t kRow = kHeads * kHeadDim / 4;      // 8-byte groups per chunk partial
@@ -455,36 +465,57 @@ __global__ __launch_bounds__(64) void mfa_combine_kernel(const AttnArgs p) {
         return f32x4{__builtin_bit_cast(float, d.x << 16), __builtin_bit_cast(float, d.x & 0xffff0000u),
                      __builtin_bit_cast(float, d.y << 16), __builtin_bit_cast(float, d.y & 0xffff0000u)};
     };
+    // rows of chunks c0 .. c0 + kCombineUnroll - 1, clamped into the range
+    // (unconditional loads stay in flight together; the clamped ones are not
+    // used)
+    auto load_rows = [&](int c0, u32x2* v) {
+#pragma unroll
+        for (int j = 0; j < kCombineUnroll; j++) v[j] = po[(int64_t)min(c0 + j, c_hi - 1) * kRow];
+    };
 
-    float M = -__builtin_inff();
-    for (int c = t; c < nc; c += 64) M = fmaxf(M, lse[(int64_t)c * kHeads]);
+    u32x2 v[kCombineUnroll];
+    if (c_lo < c_hi) load_rows(c_lo, v);
+    // the maxima: this wave's range (the first 64 values kept), then the workgroup's
+    const float l0 = c_lo + t < c_hi ? lse[(int64_t)(c_lo + t) * kHeads] : -__builtin_inff();
+    float M = l0;
+    for (int c = c_lo + 64 + t; c < c_hi; c += 64) M = fmaxf(M, lse[(int64_t)c * kHeads]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (t == 0) red_m[wv] = M;
+    __syncthreads();
+    M = red_m[0];
+    for (int k = 1; k < nw; k++) M = fmaxf(M, red_m[k]);
 
     float wpart = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < nc; c0 += kCombineBlock) {
-        const int n = min(kCombineBlock, nc - c0);
-        for (int i = t; i < n; i += 64) {
-            const float wv = __builtin_amdgcn_exp2f(lse[(int64_t)(c0 + i) * kHeads] - M);
-            wts[i] = wv;
-            wpart += wv;
-        }
-        __syncthreads();
-        int i = 0;
-        for (; i + kCombineUnroll <= n; i += kCombineUnroll) {
-            u32x2 v[kCombineUnroll];
+    for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
+        const int n = min(64, c_hi - c0);
+        // lane j: the weight of chunk c0 + j (0 past the range)
+        const float lv = c0 == c_lo ? l0 : (t < n ? lse[(int64_t)(c0 + t) * kHeads] : -__builtin_inff());
+        const float wl = t < n ? __builtin_amdgcn_exp2f(lv - M) : 0.f;
+        wpart += wl;
+        for (int i = 0; i < n; i += kCombineUnroll) {
+            if (c0 != c_lo || i != 0) load_rows(c0 + i, v);
 #pragma unroll
-            for (int j = 0; j < kCombineUnroll; j++) v[j] = po[(int64_t)(c0 + i + j) * kRow];
-#pragma unroll
-            for (int j = 0; j < kCombineUnroll; j++) acc += wts[i + j] * row(v[j]);
+            for (int j = 0; j < kCombineUnroll; j++) {
+                if (i + j >= n) break;
+                const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i + j));
+                acc += wj * row(v[j]);
+            }
         }
-        for (; i < n; i++) acc += wts[i] * row(po[(int64_t)(c0 + i) * kRow]);
-        __syncthreads();
     }
-    float wsum = wpart;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
+    for (int off = 32; off >= 1; off >>= 1) wpart += __shfl_xor(wpart, off);
+    red_acc[wv][t] = acc;
+    if (t == 0) red_w[wv] = wpart;
+    __syncthreads();
+    if (wv != 0) return;
+    acc = red_acc[0][t];
+    float wsum = red_w[0];
+    for (int k = 1; k < nw; k++) {
+        acc += red_acc[k][t];
+        wsum += red_w[k];
+    }
     const float inv = 1.f / wsum;
     uint16_t* orow = p.out + ((int64_t)b * kHeads + h) * kHeadDim + 4 * t;
     *reinterpret_cast<u32x2*>(orow) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
@@ -593,7 +624,8 @@ hipError_t launch_attn_split(const AttnArgs& a, bool fp8, bool paged, int workgr
 }
 
 hipError_t launch_combine(const AttnArgs& a, int batch, const Launch& l) {
-    return launch_kernel(mfa_combine_kernel, dim3(batch * kHeads), dim3(64), l, a);
+    const int waves = std::min(kCombineWaves, std::max(1, (a.n_chunk + kCombineUnroll - 1) / kCombineUnroll));
+    return launch_kernel(mfa_combine_kernel, dim3(batch * kHeads), dim3(64 * waves), l, a);
 }
 
 hipError_t launch_gather(const KvView& kv, bool paged, int b, int max_seq_len, void* k_dst,
