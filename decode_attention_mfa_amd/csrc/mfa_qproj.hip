@@ -17,7 +17,7 @@
 // weight from HBM exactly once, so they are bandwidth-bound. Each workgroup
 // (eight waves) owns 64 output columns and a range of K; per 64-row K tile,
 // the weight tile (64 x 64) and the matching activation tile (32 or 64 rows
-// x 64) stream into an LDS ring by direct DMA, three tiles deep, every wave
+// x 64) stream into an LDS ring by direct DMA, four tiles deep, every wave
 // issuing part of each tile's DMA. Waves w and w + 4 own the same 16 columns
 // and take the two 32-row halves of each K tile; their sums are added
 // through LDS after the loop. The weight tile comes back
@@ -30,7 +30,7 @@ namespace mfa {
 
 namespace {
 
-constexpr int kGemmDepth = 3;             // K tiles in the ring
+constexpr int kGemmDepth = 4;             // K tiles in the ring
 constexpr int kTileBytes = 64 * 128;      // 64 rows x 64 bf16
 
 // 16-byte chunk positions within a 128-byte tile row. Weight rows: swizzled
