@@ -191,7 +191,12 @@ static void plan_chunks(const mfa_ctx* h, int32_t rows, int32_t qtok, int32_t ma
         return;
     }
     *nh = 1;
-    *chunk = choose_split(h, rows, max_len);
+    // multi-token decode: chunks up to the paged limit, so that the t
+    // workgroups of a sequence (one per token, side by side on one XCD) take
+    // it whole where the grid allows: no merges and fewer rounds of
+    // workgroups (t = 2 at 128 x 4096: 256 single pieces instead of 512
+    // half-length ones)
+    *chunk = choose_split(h, rows, max_len, qtok > 1 ? mfa::kMaxPagedChunkSteps * mfa::kStep : kMaxAutoSplit);
     if (h->cfg.kv_dtype == MFA_DTYPE_BF16 && qtok == 1 && max_len > 0) {
         const int64_t n = (max_len + *chunk - 1) / *chunk;
         if (4 * (int64_t)rows * n <= h->num_cu) *nh = 4;
