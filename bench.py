@@ -337,9 +337,14 @@ def main():
     attn_math = mfa.MFA_ATTN_FP8_MFMA if args.attn_math == "fp8" else mfa.MFA_ATTN_BF16_MFMA
     h = harness.create_handle(dc, split_tokens=args.split, max_context=attn_max, max_batch=dc.batch * qtok,
                               attn_math=attn_math)
-    # multi-token decode uses the chunked split, sized for batch x tokens rows
-    split = mfa.mfa_split_tokens(h, dc.batch * qtok, attn_max, attn_max if qtok > 1 else attn_min)
-    head_groups = mfa.mfa_head_groups(h, dc.batch * qtok, attn_max, attn_max if qtok > 1 else attn_min)
+    # multi-token decode: its own chunked split, one workgroup per (sequence,
+    # token, chunk)
+    if qtok > 1:
+        split = mfa.mfa_split_tokens_mtp(h, dc.batch, qtok, attn_max)
+        head_groups = 1
+    else:
+        split = mfa.mfa_split_tokens(h, dc.batch, attn_max, attn_min)
+        head_groups = mfa.mfa_head_groups(h, dc.batch, attn_max, attn_min)
     stream = torch.cuda.Stream()
     if qtok > 1:
         outs = [(torch.empty((dc.batch, qtok, 64, 256), dtype=torch.int16, device="cuda"),

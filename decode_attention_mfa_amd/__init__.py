@@ -75,6 +75,8 @@ def _load_lib():
     lib.mfa_decode_noalloc.restype = ctypes.c_int
     lib.mfa_split_tokens.argtypes = [P, I32, I32, I32]
     lib.mfa_split_tokens.restype = I32
+    lib.mfa_split_tokens_mtp.argtypes = [P, I32, I32, I32]
+    lib.mfa_split_tokens_mtp.restype = I32
     lib.mfa_head_groups.argtypes = [P, I32, I32, I32]
     lib.mfa_head_groups.restype = I32
     lib.mfa_debug_gather_kv.argtypes = [P, ctypes.POINTER(mfa_kv), I32, P, P, P]
@@ -194,6 +196,10 @@ def mfa_kv_append(h: int, x, w_k, w_v, kv: mfa_kv, batch: int, stream=None) -> N
 
 def mfa_split_tokens(h: int, batch: int, max_seq_len: int = 0, min_seq_len: int = 0) -> int:
     return _check(lib.mfa_split_tokens(h, batch, max_seq_len, min_seq_len), "mfa_split_tokens")
+
+
+def mfa_split_tokens_mtp(h: int, batch: int, num_tokens: int, max_seq_len: int = 0) -> int:
+    return _check(lib.mfa_split_tokens_mtp(h, batch, num_tokens, max_seq_len), "mfa_split_tokens_mtp")
 
 
 def mfa_head_groups(h: int, batch: int, max_seq_len: int = 0, min_seq_len: int = 0) -> int:

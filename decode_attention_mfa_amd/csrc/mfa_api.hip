@@ -398,6 +398,23 @@ int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32
     return chunk;
 }
 
+int32_t mfa_split_tokens_mtp(mfa_handle h, int32_t batch, int32_t num_tokens, int32_t max_seq_len) {
+    if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_split_tokens_mtp: not a live handle");
+    if (num_tokens < 1 || num_tokens > mfa::kMaxQueryTokens)
+        return fail(MFA_ERR_INVALID, "mfa_split_tokens_mtp: num_tokens %d outside [1, %d]", num_tokens,
+                    mfa::kMaxQueryTokens);
+    if (batch < 1 || (int64_t)batch * num_tokens > h->cfg.max_batch)
+        return fail(MFA_ERR_INVALID, "mfa_split_tokens_mtp: batch %d x num_tokens %d outside [1, max_batch %d]", batch,
+                    num_tokens, h->cfg.max_batch);
+    if (num_tokens > 1 && (h->cfg.kv_latent || h->cfg.kv_heads > 1 || h->cfg.attn_math == MFA_ATTN_FP8_MFMA))
+        return fail(MFA_ERR_UNSUPPORTED, "mfa_split_tokens_mtp: this handle decodes one token per sequence");
+    if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;
+    if (h->cfg.kv_latent) return latent_chunk(h, batch, max_seq_len);
+    int32_t chunk, nh;
+    plan_chunks(h, batch * num_tokens, num_tokens, max_seq_len, &chunk, &nh);
+    return chunk;
+}
+
 int32_t mfa_head_groups(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len) {
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_head_groups: not a live handle");
     if (max_seq_len <= 0) max_seq_len = h->cfg.max_context;

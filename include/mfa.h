@@ -240,9 +240,10 @@ int mfa_decode_noalloc(const mfa_config* cfg, const void* q, const mfa_kv* kv, v
  * -inf):
  *   q [batch][num_tokens][64][256] bf16, out [batch][num_tokens][64][256]
  *   bf16, lse_out [batch][num_tokens][64] fp32 or NULL.
- * Each cached row is fetched from HBM once for all num_tokens tokens (their
- * workgroups run side by side on one XCD and share its L2). Uses the chunked
- * split (split_tokens, or the per-call choice for batch * num_tokens rows).
+ * The workgroups of a sequence's tokens run side by side on one XCD, so most
+ * of their reads of a cached row after the first come from that XCD's L2.
+ * Uses the chunked split (split_tokens, or the per-call choice for batch *
+ * num_tokens rows that mfa_split_tokens_mtp reports).
  * 1 <= num_tokens <= 16; batch * num_tokens <= max_batch (the workspace holds
  * partials per query token). num_tokens = 1 is mfa_decode with the chunked
  * split. */
@@ -272,6 +273,17 @@ int mfa_kv_append(mfa_handle h, const void* x, const void* w_k, const void* w_v,
  * bounds kv->max_seq_len and kv->min_seq_len; 0 when it uses the balanced
  * split. */
 int32_t mfa_split_tokens(mfa_handle h, int32_t batch, int32_t max_seq_len, int32_t min_seq_len);
+
+/* The split-K chunk (tokens) mfa_decode_mtp uses for batch sequences of
+ * num_tokens query tokens each and the length bound kv->max_seq_len (always a
+ * chunked split: split_tokens if the handle fixes it, else chunks of up to
+ * 8192 tokens sized for batch * num_tokens query-row sets, so that the
+ * workgroups of a sequence's tokens take it whole where the grid allows).
+ * num_tokens = 1 gives mfa_decode's chunked split. MFA_ERR_INVALID for
+ * num_tokens outside [1, 16] or batch * num_tokens outside [1, max_batch];
+ * MFA_ERR_UNSUPPORTED for num_tokens > 1 on a handle mfa_decode_mtp rejects
+ * (latent or grouped caches, FP8-MFMA arithmetic). */
+int32_t mfa_split_tokens_mtp(mfa_handle h, int32_t batch, int32_t num_tokens, int32_t max_seq_len);
 
 /* The number of workgroups that share the 64 query heads of one (sequence,
  * chunk) in that split: 1; 2 (heads 0-31 and 32-63, which then read the same

@@ -155,6 +155,9 @@ static void sweep(const mfa_config& c) {
                         const int want = batch * t <= c.max_batch ? MFA_OK : MFA_ERR_INVALID;
                         rc = mfa_decode_mtp(h, g_dummy, &kv.kv, t, g_dummy, nullptr, batch, nullptr);
                         EXPECT(rc == want, "mtp %d x %d: %d", batch, t, rc);
+                        const int32_t sm = mfa_split_tokens_mtp(h, batch, t, ml);
+                        if (want == MFA_OK) EXPECT(sm > 0 && sm % 64 == 0 && sm <= 8192, "mtp split %d", sm);
+                        else EXPECT(sm == MFA_ERR_INVALID, "mtp split %d x %d: %d", batch, t, sm);
                     }
                 }
                 if (G == 1) {

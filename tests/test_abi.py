@@ -18,7 +18,8 @@ def _header_functions():
 def test_header_declares_the_boundary():
     names = _header_functions()
     for n in ("mfa_create", "mfa_qproj", "mfa_decode", "mfa_destroy", "mfa_status_string",
-              "mfa_last_error", "mfa_debug_gather_kv", "mfa_split_tokens", "mfa_kv_append"):
+              "mfa_last_error", "mfa_debug_gather_kv", "mfa_split_tokens", "mfa_split_tokens_mtp",
+              "mfa_kv_append"):
         assert n in names
 
 

@@ -168,3 +168,29 @@ def test_mtp_full_size_fp8():
     _say(f"    row-rel err {err.max():.3e}  lse abs err {el:.3e}")
     assert err.max() <= TOL and el <= LSE_TOL
     assert np.isfinite(o).all()
+
+
+def test_mtp_split_policy():
+    """The chunk mfa_split_tokens_mtp reports: 128 x 4096 with 2 or 4 tokens
+    per sequence takes each sequence whole (4096), one token gives
+    mfa_decode's chunked split (2048 here), a fixed split_tokens wins, and the
+    argument checks hold."""
+    m, hz = _mfa()
+    case = synth.config_case(3, batch=2, scale_len=0.25)
+    dc = hz.to_device(case)
+    h = hz.create_handle(dc, max_context=4096, max_batch=512)
+    try:
+        assert m.mfa_split_tokens_mtp(h, 128, 2, 4096) == 4096
+        assert m.mfa_split_tokens_mtp(h, 128, 4, 4096) == 4096
+        assert m.mfa_split_tokens_mtp(h, 128, 1, 4096) == 2048
+        assert m.mfa_split_tokens_mtp(h, 8, 2, 1000) == 256   # the smallest automatic chunk
+        for bad in ((128, 0, 4096), (128, 17, 4096), (0, 2, 4096), (300, 2, 4096)):
+            with pytest.raises(RuntimeError):
+                m.mfa_split_tokens_mtp(h, *bad)
+    finally:
+        m.mfa_destroy(h)
+    h = hz.create_handle(dc, split_tokens=512, max_context=4096, max_batch=512)
+    try:
+        assert m.mfa_split_tokens_mtp(h, 128, 2, 4096) == 512
+    finally:
+        m.mfa_destroy(h)
