@@ -223,6 +223,44 @@ def cpu_baseline(case, budget_s: float, gpu_out=None, gpu_lse=None):
     return res
 
 
+def context_rates(mfa, torch) -> dict:
+    """Rates measured on this GPU to set beside the data-sheet peaks that the
+    roofline and MFMA fractions divide by: a device copy of 1 GiB (bytes read
+    plus bytes written over its time) and the matrix-core microbenchmark
+    (mfa_debug_mfma_rate) for the two MFMA shapes the path uses."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        dst.copy_(src)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    rates = {}
+    for kind, name in ((0, "bf16"), (1, "fp8")):
+        iters = 1 << 14
+        mfa.mfa_debug_mfma_rate(kind, iters, sink)   # warm-up
+        fl = 0.0
+        e0.record()
+        for _ in range(5):
+            fl += mfa.mfa_debug_mfma_rate(kind, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        rates[name] = round(fl / (e0.elapsed_time(e1) / 1e3) / 1e12, 1)
+    return {"stream_copy_gbps": round(copy_gbps, 1),
+            "stream_copy": "device copy of 1 GiB, (read + written bytes) / time, 10 copies",
+            "mfma_rate_tflops": rates,
+            "mfma_rate": "mfa_debug_mfma_rate: independent v_mfma_f32_16x16x32_bf16 / unit-scaled "
+                         "v_mfma_f32_16x16x128_f8f6f4 on register operands, two waves per SIMD, 5 launches"}
+
+
 def traffic_key(workload: str, attn_math: str) -> str:
     """Key of a workload's stored HBM counters (per attention arithmetic)."""
     return workload if attn_math == "bf16" else f"{workload}/{attn_math}"
@@ -265,6 +303,8 @@ def main():
     ap.add_argument("--attn-math", default="bf16", choices=("bf16", "fp8"),
                     help="attention arithmetic: bf16 MFMAs (default) or FP8 MFMAs (FP8 caches only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline budget; 0 skips it")
+    ap.add_argument("--context", type=int, default=1,
+                    help="1 (default): also measure a device copy and the MFMA rate microbenchmark")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -491,6 +531,9 @@ def main():
         result["kv_append"] = {"algorithmic_bytes": ab, "kernels_us": round(app_us, 2),
                                "achieved_gbps": round(ab / (app_us / 1e6) / 1e9, 1),
                                "frac": round(ab / (app_us / 1e6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    if args.context:
+        log("[bench] context: device copy and matrix-core rates")
+        result["context"] = context_rates(mfa, torch)
     if args.cpu_seconds > 0:
         log("[bench] timing the fp64 CPU oracle on a bounded sample")
         o_last, l_last = outs[(args.steps - 1) % nrot]

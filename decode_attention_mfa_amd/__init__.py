@@ -83,6 +83,8 @@ def _load_lib():
     lib.mfa_debug_gather_kv.restype = ctypes.c_int
     lib.mfa_debug_fp8_mfma.argtypes = [P, P, P, P, I32, P]
     lib.mfa_debug_fp8_mfma.restype = ctypes.c_int
+    lib.mfa_debug_mfma_rate.argtypes = [I32, I32, P, P, P]
+    lib.mfa_debug_mfma_rate.restype = ctypes.c_int
     lib.mfa_profile_enable.argtypes = [P, ctypes.c_int]
     lib.mfa_profile_enable.restype = ctypes.c_int
     lib.mfa_profile_read.argtypes = [P, P, P]
@@ -216,6 +218,15 @@ def mfa_debug_fp8_mfma(a, b, c, d, n_tiles: int, stream=None) -> None:
     b [n,128,16] E4M3 codes; c (or None), d [n,16,16] fp32)."""
     _check(lib.mfa_debug_fp8_mfma(_ptr(a), _ptr(b), _ptr(c), _ptr(d), n_tiles, _stream(stream)),
            "mfa_debug_fp8_mfma")
+
+
+def mfa_debug_mfma_rate(kind: int, iters: int, sink, stream=None) -> float:
+    """Launch the matrix-core rate microbenchmark (kind 0: bf16 16x16x32
+    MFMAs, 1: E4M3 16x16x128) on the stream; returns the launch's flop count."""
+    flops = ctypes.c_double(0.0)
+    _check(lib.mfa_debug_mfma_rate(kind, iters, _ptr(sink), ctypes.byref(flops), _stream(stream)),
+           "mfa_debug_mfma_rate")
+    return flops.value
 
 
 def mfa_profile_enable(h: int, enable: bool = True) -> None:

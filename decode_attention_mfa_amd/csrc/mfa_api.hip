@@ -774,6 +774,23 @@ int mfa_debug_fp8_mfma(const void* a, const void* b, const float* c, float* d, i
     return MFA_OK;
 }
 
+int mfa_debug_mfma_rate(int32_t kind, int32_t iters, float* sink, double* flops, void* hip_stream) {
+    g_last_error[0] = 0;
+    if (kind != 0 && kind != 1) return fail(MFA_ERR_INVALID, "mfa_debug_mfma_rate: kind %d is not 0 or 1", kind);
+    if (iters < 1 || iters > (1 << 24))
+        return fail(MFA_ERR_INVALID, "mfa_debug_mfma_rate: iters %d outside [1, 2^24]", iters);
+    if (!sink || !flops) return fail(MFA_ERR_INVALID, "mfa_debug_mfma_rate: null sink or flops");
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "mfa_debug_mfma_rate: device query");
+    const int workgroups = 2 * ncu;   // two waves per SIMD
+    *flops = mfa::mfma_rate_flops(kind, iters, workgroups);
+    e = mfa::launch_mfma_rate(kind, iters, workgroups, sink, mfa::Launch{(hipStream_t)hip_stream});
+    if (e != hipSuccess) return hip_fail(e, "mfa_debug_mfma_rate: launch");
+    return MFA_OK;
+}
+
 int mfa_profile_enable(mfa_handle h, int enable) {
     g_last_error[0] = 0;
     if (!valid_handle(h)) return fail(MFA_ERR_INVALID, "mfa_profile_enable: not a live handle");

@@ -88,6 +88,11 @@ hipError_t launch_fill_zero(uint32_t* p, size_t n, const Launch& l);
 // mode runs them: d = a . b + c per tile (c may be null: zero)
 hipError_t launch_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d, int n_tiles,
                            const Launch& l);
+// the matrix-core rate microbenchmark (kind 0: bf16 16x16x32, 1: E4M3
+// 16x16x128): `workgroups` of four waves, each running `iters` rounds of
+// independent MFMAs on register operands; the flops of such a launch
+hipError_t launch_mfma_rate(int kind, int iters, int workgroups, float* sink, const Launch& l);
+double mfma_rate_flops(int kind, int iters, int workgroups);
 
 struct QprojArgs {
     const uint16_t* x;      // [B][hidden]

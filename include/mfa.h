@@ -312,6 +312,20 @@ int mfa_debug_gather_kv(mfa_handle h, const mfa_kv* kv, int32_t b, void* k_dst, 
 int mfa_debug_fp8_mfma(const void* a, const void* b, const float* c, float* d, int32_t n_tiles,
                        void* hip_stream);
 
+/* Measurement support: the matrix-core rate microbenchmark, to set the MFMA
+ * rates the attention reaches beside what the chip sustains. One launch of
+ * two workgroups of four waves per compute unit (two waves per SIMD); each
+ * wave runs iters rounds of eight independent MFMAs on operands held in
+ * registers, with no memory traffic: kind 0 v_mfma_f32_16x16x32_bf16 (the
+ * bf16 MFMA of the attention and the Q projection), kind 1 the unit-scaled
+ * v_mfma_f32_16x16x128_f8f6f4 on E4M3 codes (the FP8-MFMA mode). *flops
+ * (host) receives the launch's floating-point operations (2 per
+ * multiply-add); dividing by its duration gives the rate. sink is a device
+ * float the kernel may write (it never does for these operands; the write
+ * keeps the work). No handle; 1 <= iters <= 2^24 (about 7 ms per 2^16 on
+ * MI355X). Asynchronous on hip_stream. */
+int mfa_debug_mfma_rate(int32_t kind, int32_t iters, float* sink, double* flops, void* hip_stream);
+
 /* Kernel kinds reported by mfa_profile_read. */
 enum mfa_kernel_kind {
     MFA_KERNEL_ATTENTION = 0,   /* chunked decode attention */

@@ -298,6 +298,20 @@ static void noalloc_limits() {
     EXPECT(mfa_decode_noalloc(nullptr, g_dummy, &kv.kv, g_dummy, nullptr, 1, nullptr) == MFA_ERR_INVALID, "null cfg");
 }
 
+// the matrix-core rate microbenchmark: argument checks and the flop count
+static void mfma_rate() {
+    double fl = 0;
+    for (int kind : {0, 1}) {
+        EXPECT(mfa_debug_mfma_rate(kind, 100, (float*)g_dummy, &fl, nullptr) == MFA_OK, "mfma rate kind %d", kind);
+        EXPECT(fl == 2.0 * 256 * 4 * 100 * 8 * 2 * 16 * 16 * (kind == 0 ? 32 : 128), "mfma rate flops %g", fl);
+    }
+    EXPECT(mfa_debug_mfma_rate(2, 100, (float*)g_dummy, &fl, nullptr) == MFA_ERR_INVALID, "mfma rate kind 2");
+    EXPECT(mfa_debug_mfma_rate(0, 0, (float*)g_dummy, &fl, nullptr) == MFA_ERR_INVALID, "mfma rate iters 0");
+    EXPECT(mfa_debug_mfma_rate(0, (1 << 24) + 1, (float*)g_dummy, &fl, nullptr) == MFA_ERR_INVALID, "mfma rate iters");
+    EXPECT(mfa_debug_mfma_rate(0, 100, nullptr, &fl, nullptr) == MFA_ERR_INVALID, "mfma rate null sink");
+    EXPECT(mfa_debug_mfma_rate(0, 100, (float*)g_dummy, nullptr, nullptr) == MFA_ERR_INVALID, "mfma rate null flops");
+}
+
 // handles created, used and destroyed on several threads at once
 static void threads() {
     std::vector<std::thread> ts;
@@ -368,6 +382,7 @@ int main(int argc, char** argv) {
         stale_handles();
         allocation_failures();
         noalloc_limits();
+        mfma_rate();
     }
     threads();
     EXPECT(stub_live_allocations() == 0, "%ld workspace blocks never freed", stub_live_allocations());

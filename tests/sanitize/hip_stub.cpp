@@ -204,6 +204,14 @@ hipError_t launch_fp8_mfma(const uint8_t* a, const uint8_t* b, const float*, flo
     g_launches++;
     return hipSuccess;
 }
+hipError_t launch_mfma_rate(int kind, int iters, int workgroups, float* sink, const Launch&) {
+    if ((kind != 0 && kind != 1) || iters < 1 || workgroups < 1 || !sink) die("launch_mfma_rate", nullptr, 0);
+    g_launches++;
+    return hipSuccess;
+}
+double mfma_rate_flops(int kind, int iters, int workgroups) {
+    return (double)workgroups * 4 * iters * 8 * 2.0 * 16 * 16 * (kind == 0 ? 32 : 128);
+}
 hipError_t launch_qproj_down(const QprojArgs& a, const Launch&) {
     if (a.ksplit < 1 || a.hidden % (64 * a.ksplit) || a.hidden / a.ksplit < kQprojRowsPerSplit)
         die("launch_qproj_down: ksplit", nullptr, 0);
