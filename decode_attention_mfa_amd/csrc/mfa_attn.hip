@@ -114,8 +114,12 @@ __device__ __forceinline__ const uint8_t* wave_uniform(const uint8_t* ptr) {
 // per-XCD L2, so a workgroup on another XCD sees the data once the store is
 // acknowledged. The loads are issued as one asm block that also waits for
 // them, so no output register is left pending when the block ends.
+// A store of more than 8 bytes still reads its data VGPRs after it issues: a
+// VALU write to them must come at least two wait states later on this
+// architecture. The compiler keeps that distance after the stores it
+// generates but cannot see this one, so the block ends with the wait states.
 __device__ __forceinline__ void coherent_store_b128(u32x4* ptr, u32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(ptr), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(ptr), "v"(v) : "memory");
 }
 __device__ __forceinline__ void coherent_load_b128x8(f32x4* v, const f32x4* src, int stride) {
     asm volatile(
