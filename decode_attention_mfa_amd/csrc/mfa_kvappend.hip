@@ -45,6 +45,10 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float f) {
 // Block b: sequence b. Row L_b is written when L_b >= 0 and the row exists:
 // contiguous, L_b < kv_stride; paged, the page-table slot L_b / 64 exists and
 // names a page in [0, num_pages). Otherwise nothing is written.
+// K splits whose partials are loaded all at once (7168 / 256 = 28 at the
+// model's hidden size)
+constexpr int kWriteBatch = 32;
+
 template <bool FP8, bool PAGED>
 __global__ __launch_bounds__(256) void mfa_kv_write_kernel(KvAppendArgs a) {
     const int b = blockIdx.x;
@@ -66,6 +70,24 @@ __global__ __launch_bounds__(256) void mfa_kv_write_kernel(KvAppendArgs a) {
     const float* vp = kp + a.ksplit * plane;
     float ks = 0.f, vs = 0.f;
     int s = 0;
+    if (a.ksplit <= kWriteBatch) {
+        // every partial of this column requested before the first is added:
+        // one memory round trip; the sums still run in split order
+        float kr[kWriteBatch], vr[kWriteBatch];
+#pragma unroll
+        for (int u = 0; u < kWriteBatch; u++) {
+            kr[u] = u < a.ksplit ? kp[u * plane] : 0.f;
+            vr[u] = u < a.ksplit ? vp[u * plane] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kWriteBatch; u++) {
+            if (u < a.ksplit) {
+                ks += kr[u];
+                vs += vr[u];
+            }
+        }
+        s = a.ksplit;
+    }
     for (; s + 8 <= a.ksplit; s += 8) {
         float kr[8], vr[8];
 #pragma unroll
